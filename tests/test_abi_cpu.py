@@ -1,0 +1,133 @@
+"""Host-side checks of the C ABI (no GPU needed, no compute launched).
+
+- libdsa.so / libdsa_calib.so load and export every function include/*.h declares;
+- every invalid argument is rejected on the host with its status code before
+  anything is enqueued (fake device pointers are never dereferenced);
+- the workspace size and the automatic plan are pure host arithmetic.
+"""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from sparse_attention_kv_dsa_amd import build as dsa_build
+from sparse_attention_kv_dsa_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
+FAKE = 0x10000          # 4096-aligned, never dereferenced by a rejected call
+FAKE2 = 0x20000
+
+
+def _declared(path):
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(dsa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_headers_exist():
+    names = [os.path.basename(h) for h in HEADERS]
+    assert "dsa.h" in names and "dsa_calib.h" in names
+
+
+@pytest.mark.parametrize("header,lib", [("dsa.h", "libdsa.so"), ("dsa_calib.h", "libdsa_calib.so")])
+def test_library_exports_every_declared_symbol(header, lib):
+    path = dsa_build.lib_path(lib)
+    assert os.path.exists(path), f"{lib} not built"
+    L = ctypes.CDLL(path)
+    decl = _declared(os.path.join(ROOT, "include", header))
+    assert decl, header
+    for name in decl:
+        assert hasattr(L, name), f"{lib} does not export {name}"
+
+
+def test_status_strings():
+    assert [B.status_string(i) for i in range(5)] == [
+        "DSA_OK", "DSA_ERR_INVALID_ARG", "DSA_ERR_UNSUPPORTED", "DSA_ERR_WORKSPACE", "DSA_ERR_HIP"]
+    assert B.status_string(99) == "unknown"
+
+
+def test_workspace_bytes():
+    L = B.lib()
+    # 64 rows -> 256 B of counters; 64 x 512 keys
+    assert L.dsa_select_workspace_bytes(64, 32768, 64, 32) == 256 + 64 * 512 * 4
+    assert L.dsa_select_workspace_bytes(65, 100, 7, 3) == 512 + 65 * 15 * 4
+    assert L.dsa_select_workspace_bytes(0, 100, 7, 3) == 0
+    assert L.dsa_select_workspace_bytes(5, 0, 7, 3) == 0
+    assert L.dsa_select_workspace_bytes(5, 100, 0, 3) == 0
+    assert L.dsa_select_workspace_bytes(5, 100, 4, -1) == 0
+
+
+def test_auto_plan():
+    assert B.select_plan(4096, 16384, 64, 32)[0] == 1      # many rows: a workgroup per row
+    assert B.select_plan(8192, 65536, 64, 64)[0] == 1
+    assert B.select_plan(8, 1000, 64, 4)[0] == 1           # one chunk per row anyway
+    p, cb = B.select_plan(64, 32768, 64, 32)               # few long rows: split
+    assert p == 2 and cb % 4 == 0 and cb >= 1
+    p, cb = B.select_plan(128, 131072, 128, 16)
+    assert p == 2 and cb % 2 == 0
+
+
+def _sel(**kw):
+    a = dict(logits=FAKE, rows=4, width=64, ld=64, ks=None, ke=FAKE, k=4, B=8, R=1, out=FAKE2,
+             ld_out=4, scores=None, ld_scores=0, ws=FAKE, ws_bytes=1 << 20, plan=0, cb=0)
+    a.update(kw)
+    return B.lib().dsa_select_candidate_blocks_plan(
+        a["logits"], a["rows"], a["width"], a["ld"], a["ks"], a["ke"], a["k"], a["B"], a["R"],
+        a["out"], a["ld_out"], a["scores"], a["ld_scores"], a["ws"], a["ws_bytes"], a["plan"],
+        a["cb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rows=-1), 1), (dict(width=-1), 1), (dict(B=0), 1), (dict(R=0), 1), (dict(k=-1), 1),
+    (dict(ld=63), 1), (dict(ld_out=3), 1), (dict(plan=3), 1), (dict(plan=-1), 1), (dict(cb=-1), 1),
+    (dict(scores=FAKE, ld_scores=7), 1),         # nblocks = 8
+    (dict(out=None), 1), (dict(out=FAKE2 + 2), 1), (dict(logits=None), 1), (dict(ke=None), 1),
+    (dict(logits=FAKE + 2), 1), (dict(scores=FAKE + 1, ld_scores=8), 1),
+    (dict(ws=None), 3), (dict(ws_bytes=100), 3), (dict(ws=FAKE + 2), 3),
+    (dict(width=1 << 20, ld=1 << 20, B=16, k=4096, ld_out=4096), 2),  # keys do not fit in LDS
+    (dict(rows=0), 0), (dict(k=0), 0), (dict(rows=0, logits=None, ke=None, out=None), 0),
+])
+def test_select_rejects_on_host(kw, code):
+    assert _sel(**kw) == code
+
+
+def _bs(**kw):
+    a = dict(logits=FAKE, rows=4, width=64, ld=64, ks=None, ke=FAKE, B=8, R=1, pin=1,
+             scores=FAKE2, ld_scores=8)
+    a.update(kw)
+    return B.lib().dsa_block_scores(a["logits"], a["rows"], a["width"], a["ld"], a["ks"],
+                                    a["ke"], a["B"], a["R"], a["pin"], a["scores"],
+                                    a["ld_scores"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rows=-1), 1), (dict(width=-1), 1), (dict(B=0), 1), (dict(R=0), 1), (dict(pin=2), 1),
+    (dict(ld=10), 1), (dict(ld_scores=7), 1), (dict(logits=None), 1), (dict(ke=None), 1),
+    (dict(scores=None), 1), (dict(logits=FAKE + 1), 1), (dict(scores=FAKE2 + 3), 1),
+    (dict(rows=0), 0), (dict(width=0, ld_scores=0), 0),
+])
+def test_block_scores_rejects_on_host(kw, code):
+    assert _bs(**kw) == code
+
+
+def test_calib_rejects_on_host():
+    L = ctypes.CDLL(dsa_build.lib_path("libdsa_calib.so"))
+    L.dsa_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.dsa_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    assert L.dsa_calib_copy(FAKE, FAKE2, 17, None) == 1
+    assert L.dsa_calib_copy(FAKE + 4, FAKE2, 16, None) == 1
+    assert L.dsa_calib_copy(None, FAKE2, 16, None) == 1
+    assert L.dsa_calib_copy(FAKE, FAKE2, 0, None) == 0
+    assert L.dsa_calib_read(FAKE, 16, None, None) == 1
+    assert L.dsa_calib_read_sink_words() >= 1
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 64)
+    with pytest.raises(ValueError):
+        B.select_candidate_blocks(x, None, torch.zeros(4, dtype=torch.int32), 4, 8,
+                                  torch.zeros(4, 4, dtype=torch.int32))

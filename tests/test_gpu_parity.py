@@ -1,0 +1,351 @@
+"""GPU parity: the HIP library against the CPU oracle, element by element.
+
+Block ids (values and order) must match exactly; block scores must match bit
+for bit (the max is exact, NaN is the canonical 0x7FC00000).  Inputs come from
+the seeded generators in sparse_attention_kv_dsa_amd.workloads; expected
+values come only from oracle/.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_kv_dsa_amd as dsa
+from sparse_attention_kv_dsa_amd import workloads
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def dev_logits(x: np.ndarray, ld_pad: int = 0, offset: int = 0, pad_value=np.nan):
+    """Copy [rows, width] to the GPU with row stride width+ld_pad, starting
+    `offset` floats into the allocation; the padding holds `pad_value`, so a
+    read outside a row's first `width` columns would show up in the results."""
+    rows, width = x.shape
+    ld = width + ld_pad
+    flat = torch.full((offset + rows * ld + 4,), float(pad_value), dtype=torch.float32, device=DEV)
+    view = flat[offset:offset + rows * ld].view(rows, ld) if rows else flat[:0].view(0, ld)
+    if rows and width:
+        view[:, :width].copy_(torch.from_numpy(np.ascontiguousarray(x)))
+    return view[:, :width]
+
+
+def dev_i32(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
+
+
+def gpu_select(w, plan=0, cb=0, ld_pad=0, offset=0, with_scores=True, ld_out_pad=0):
+    x = dev_logits(w.logits, ld_pad, offset)
+    nb = -(-w.width // w.block_size)
+    out_full = torch.full((w.rows, w.topk_blocks + ld_out_pad), 12345, dtype=torch.int32, device=DEV)
+    out = out_full[:, :w.topk_blocks]
+    sc = None
+    if with_scores:
+        sc = torch.full((w.rows, max(nb, 1)), 777.0, dtype=torch.float32, device=DEV)[:, :nb]
+    dsa.select_candidate_blocks(x, dev_i32(w.row_ks), dev_i32(w.row_ke), w.topk_blocks,
+                                w.block_size, out, w.row_repeat, scores_out=sc, plan=plan,
+                                chunk_blocks=cb)
+    torch.cuda.synchronize()
+    if ld_out_pad:
+        assert (out_full[:, w.topk_blocks:] == 12345).all(), "wrote past topk_blocks"
+    return out.cpu().numpy(), (None if sc is None else sc.cpu().numpy())
+
+
+def oracle_select(w, rows=None):
+    nb = -(-w.width // w.block_size)
+    out = np.empty((w.rows, w.topk_blocks), dtype=np.int32)
+    sc = np.empty((w.rows, nb), dtype=np.float32)
+    oracle.select_candidate_blocks(w.logits, w.row_ks, w.row_ke, w.topk_blocks, w.block_size,
+                                   out, w.row_repeat, scores_out=sc if nb else None, nthreads=8)
+    return out, sc
+
+
+def assert_same(got_out, got_sc, exp_out, exp_sc, ctx=""):
+    if not np.array_equal(got_out, exp_out):
+        bad = np.argwhere(got_out != exp_out)
+        r = bad[0][0]
+        raise AssertionError(f"{ctx}: ids differ in {len(np.unique(bad[:, 0]))} rows; first row {r}:"
+                             f"\n gpu    {got_out[r].tolist()}\n oracle {exp_out[r].tolist()}")
+    if got_sc is not None and exp_sc is not None and exp_sc.size:
+        gb, eb = got_sc.view(np.uint32), exp_sc.view(np.uint32)
+        if not np.array_equal(gb, eb):
+            bad = np.argwhere(gb != eb)
+            r, b = bad[0]
+            raise AssertionError(f"{ctx}: scores differ at {len(bad)} places; first [{r},{b}]: "
+                                 f"gpu {gb[r, b]:#010x} oracle {eb[r, b]:#010x}")
+
+
+# ------------------------------------------------------------------ small ---
+
+GOLDEN_CASES = None
+
+
+def _golden():
+    import json
+    import os
+    global GOLDEN_CASES
+    if GOLDEN_CASES is None:
+        with open(os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")) as fh:
+            GOLDEN_CASES = json.load(fh)["cases"]
+    return GOLDEN_CASES
+
+
+def _golden_workload(c):
+    conv = {"nan": np.nan, "inf": np.inf, "-inf": -np.inf, "-0": -0.0}
+    width = len(c["logits"][0])
+    x = np.array([[conv[v] if isinstance(v, str) else float(v) for v in r] for r in c["logits"]],
+                 dtype=np.float32).reshape(len(c["logits"]), width)
+    ks = None if c["row_ks"] is None else np.array(c["row_ks"], np.int32)
+    return workloads.Workload(c["id"], x, ks, np.array(c["row_ke"], np.int32), c["block_size"],
+                              c["topk"], c["row_repeat"])
+
+
+@pytest.mark.parametrize("plan,cb", [(1, 0), (2, 1), (2, 2)])
+def test_hand_worked_rows(plan, cb):
+    for c in _golden():
+        w = _golden_workload(c)
+        got, sc = gpu_select(w, plan, cb)
+        assert got.tolist() == c["out"], c["id"]
+        exp_out, exp_sc = oracle_select(w)
+        assert_same(got, sc, exp_out, exp_sc, c["id"])
+
+
+@pytest.mark.parametrize("plan", [1, 2])
+def test_random_tiny_cases(plan):
+    """400 tiny cases: NaN, +-0, +-inf, ties, odd widths and block sizes,
+    negative/overlong/empty windows, row_repeat 1-3, k 0-12."""
+    for seed in range(400):
+        w = workloads.random_case(seed, ld_pad=seed % 5)
+        cb = 1 + seed % 3
+        got, sc = gpu_select(w, plan, cb, ld_pad=seed % 5, offset=seed % 4)
+        exp_out, exp_sc = oracle_select(w)
+        assert_same(got, sc, exp_out, exp_sc, f"seed {seed} plan {plan} cb {cb} {w.describe()}")
+
+
+MEDIUM_B = [1, 3, 4, 5, 8, 12, 16, 32, 64, 100, 128, 256, 512]
+
+
+@pytest.mark.parametrize("plan", [1, 2])
+def test_random_medium_cases(plan):
+    """Several tiles per row and ragged tails, aligned (vector) and unaligned
+    (scalar) rows, both launch plans with assorted chunk sizes."""
+    rng = np.random.default_rng(7 + plan)
+    for i in range(60):
+        rows = int(rng.integers(1, 41))
+        width = int(rng.integers(1, 6001))
+        if i % 3 == 0:
+            width = (width // 4) * 4 + 4
+        B = int(MEDIUM_B[i % len(MEDIUM_B)])
+        R = int(rng.integers(1, 4))
+        k = int(rng.integers(0, 101))
+        g = -(-rows // R)
+        vals = rng.standard_normal((rows, width)).astype(np.float32)
+        if i % 2:
+            vals = np.round(vals * 2) / 2        # ties
+            vals[rng.random((rows, width)) < 0.01] = np.nan
+            vals[rng.random((rows, width)) < 0.02] = -np.inf
+        ks = None
+        if i % 4 == 1:
+            ks = (rng.integers(0, width // 4 + 1, size=g) * 4).astype(np.int32)
+        elif i % 4 == 3:
+            ks = rng.integers(-5, width + 5, size=g).astype(np.int32)
+        base = ks if ks is not None else np.zeros(g, np.int32)
+        ke = np.clip(base + rng.integers(-10, width + 10, size=g), -3, width + 9).astype(np.int32)
+        w = workloads.Workload(f"medium-{i}", vals, ks, ke, B, k, R)
+        ld_pad = [0, 0, 4, 1, 3][i % 5]
+        offset = [0, 0, 0, 4, 1][i % 5]
+        cb = int(rng.integers(1, 40))
+        got, sc = gpu_select(w, plan, cb, ld_pad=ld_pad, offset=offset, ld_out_pad=3)
+        exp_out, exp_sc = oracle_select(w)
+        assert_same(got, sc, exp_out, exp_sc, f"case {i} plan {plan} cb {cb} {w.describe()}")
+
+
+@pytest.mark.parametrize("pin", [True, False])
+def test_block_scores(pin):
+    rng = np.random.default_rng(21)
+    for i in range(80):
+        w = workloads.random_case(500 + i, max_rows=9, max_width=3000, max_block=300,
+                                  special=i % 2 == 0, ld_pad=i % 3)
+        x = dev_logits(w.logits, i % 3, offset=(i % 2) * 4)
+        got = dsa.block_scores(x, dev_i32(w.row_ks), dev_i32(w.row_ke), w.block_size,
+                               w.row_repeat, pin_newest=pin)
+        torch.cuda.synchronize()
+        exp = oracle.block_scores(w.logits, w.row_ks, w.row_ke, w.block_size, w.row_repeat,
+                                  pin_newest=pin)
+        assert_same(np.zeros(1), got.cpu().numpy(), np.zeros(1), exp, f"block_scores {i}")
+    del rng
+
+
+def test_block_scores_configs():
+    for i in (1, 2, 4):
+        w = workloads.config(i)
+        _say("block scores", w.name)
+        x = dev_logits(w.logits)
+        for pin in (True, False):
+            got = dsa.block_scores(x, dev_i32(w.row_ks), dev_i32(w.row_ke), w.block_size,
+                                   w.row_repeat, pin_newest=pin).cpu().numpy()
+            exp = oracle.block_scores(w.logits, w.row_ks, w.row_ke, w.block_size, w.row_repeat,
+                                      pin_newest=pin, nthreads=8)
+            assert_same(np.zeros(1), got, np.zeros(1), exp, f"{w.name} pin={pin}")
+
+
+# ---------------------------------------------------------------- configs ---
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_config_full(cfg):
+    w = workloads.config(cfg)
+    _say("config", cfg, w.name, "plan", dsa.select_plan(w.rows, w.width, w.block_size,
+                                                          w.topk_blocks))
+    exp_out, exp_sc = oracle_select(w)
+    got, sc = gpu_select(w)
+    assert_same(got, sc, exp_out, exp_sc, w.name)
+    # the other plan gives the same bits
+    auto = dsa.select_plan(w.rows, w.width, w.block_size, w.topk_blocks)[0]
+    got2, sc2 = gpu_select(w, plan=3 - auto)
+    assert_same(got2, sc2, exp_out, exp_sc, w.name + " other plan")
+
+
+def _check_properties(out, nblocks):
+    for r in range(out.shape[0]):
+        row = out[r]
+        ids = row[row >= 0]
+        n = len(ids)
+        assert (row[n:] == -1).all(), r
+        assert len(np.unique(ids)) == n and (ids < nblocks).all(), r
+
+
+def test_config5_sampled_rows():
+    """Large prefill at full size (2 GiB of logits) in the launch plan the
+    benchmark times: every row checked for valid ids, 96 sampled rows (both
+    requests, first/last rows) against the oracle, including their scores."""
+    w = workloads.config(5)
+    _say("config 5 generated", w.name)
+    got, sc = gpu_select(w)
+    nb = -(-w.width // w.block_size)
+    _check_properties(got, nb)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, 4095, 4096, 4097, 8191],
+                                     rng.choice(8192, size=90, replace=False)]))
+    sub = workloads.Workload(w.name, np.ascontiguousarray(w.logits[rows]), w.row_ks[rows].copy(),
+                             w.row_ke[rows].copy(), w.block_size, w.topk_blocks, 1)
+    exp_out, exp_sc = oracle_select(sub)
+    assert_same(got[rows], sc[rows], exp_out, exp_sc, "config 5 sampled rows")
+    # heavy ties: many selected rows end in a run of equal scores, broken by ascending id
+    s_sel = np.take_along_axis(sc[rows], np.maximum(exp_out, 0), axis=1)
+    assert (s_sel[:, -1] == s_sel[:, -2]).mean() > 0.5
+
+
+# ------------------------------------------------------------ behaviour ----
+
+def test_degenerate_shapes():
+    out = torch.full((3, 4), 7, dtype=torch.int32, device=DEV)
+    ke = torch.zeros(3, dtype=torch.int32, device=DEV)
+    dsa.select_candidate_blocks(torch.empty((3, 0), device=DEV), None, ke, 4, 8, out)
+    torch.cuda.synchronize()
+    assert (out == -1).all()                       # width == 0 -> -1
+    out.fill_(7)
+    dsa.select_candidate_blocks(torch.empty((0, 10), device=DEV), None, ke, 4, 8, out[:0])
+    dsa.select_candidate_blocks(torch.ones((3, 10), device=DEV), None, ke + 10, 0, 8, out[:, :0])
+    torch.cuda.synchronize()
+    assert (out == 7).all()                        # rows == 0 / topk == 0 write nothing
+
+
+def test_errors_write_nothing():
+    x = torch.ones((4, 64), device=DEV)
+    ke = torch.full((4,), 64, dtype=torch.int32, device=DEV)
+    out = torch.full((4, 4), 7, dtype=torch.int32, device=DEV)
+    for kwargs in (dict(block_size=0), dict(row_repeat=0)):
+        args = dict(block_size=8, row_repeat=1)
+        args.update(kwargs)
+        with pytest.raises(dsa.DsaError) as e:
+            dsa.select_candidate_blocks(x, None, ke, 4, args["block_size"], out, args["row_repeat"])
+        assert e.value.code == 1
+    with pytest.raises(dsa.DsaError) as e:
+        dsa.select_candidate_blocks(x, None, ke, 5, 8, out)   # ld_out < topk
+    assert e.value.code == 1
+    big = torch.ones((1, 1 << 18), device=DEV)
+    with pytest.raises(dsa.DsaError) as e:                    # 65536 keys exceed LDS
+        dsa.select_candidate_blocks(big, None, ke[:1], 4, 4, out[:1])
+    assert e.value.code == 2
+    ws = dsa.Workspace(DEV, 64)
+    lib = dsa.lib()
+    code = lib.dsa_select_candidate_blocks(x.data_ptr(), 4, 64, 64, None, ke.data_ptr(), 4, 8, 1,
+                                           out.data_ptr(), 4, None, 0, ws.buf.data_ptr(), 64,
+                                           torch.cuda.current_stream().cuda_stream)
+    assert code == 3
+    torch.cuda.synchronize()
+    assert (out == 7).all()
+
+
+def test_repeat_calls_bit_identical_and_workspace_restored():
+    w = workloads.config(2)
+    x = dev_logits(w.logits)
+    ks, ke = dev_i32(w.row_ks), dev_i32(w.row_ke)
+    ws = dsa.Workspace(DEV)
+    first = None
+    for plan, cb in ((2, 0), (2, 4), (1, 0)):
+        for _ in range(50):
+            out = torch.empty((w.rows, w.topk_blocks), dtype=torch.int32, device=DEV)
+            dsa.select_candidate_blocks(x, ks, ke, w.topk_blocks, w.block_size, out, w.row_repeat,
+                                        workspace=ws, plan=plan, chunk_blocks=cb)
+            o = out.cpu().numpy()
+            if first is None:
+                first = o
+            assert np.array_equal(o, first)
+        counters = ws.buf[: 4 * w.rows].view(torch.int32)
+        assert int(counters.abs().sum()) == 0, "arrival counters not reset"
+    exp_out, _ = oracle_select(w)
+    assert np.array_equal(first, exp_out)
+
+
+def test_two_streams_two_workspaces():
+    wa, wb = workloads.config(2), workloads.config(4)
+    exp_a, _ = oracle_select(wa)
+    exp_b, _ = oracle_select(wb)
+    xa, xb = dev_logits(wa.logits), dev_logits(wb.logits)
+    sa, sb = torch.cuda.Stream(DEV), torch.cuda.Stream(DEV)
+    wsa, wsb = dsa.Workspace(DEV), dsa.Workspace(DEV)
+    outs_a, outs_b = [], []
+    torch.cuda.synchronize()
+    for _ in range(20):
+        oa = torch.empty((wa.rows, wa.topk_blocks), dtype=torch.int32, device=DEV)
+        ob = torch.empty((wb.rows, wb.topk_blocks), dtype=torch.int32, device=DEV)
+        with torch.cuda.stream(sa):
+            dsa.select_candidate_blocks(xa, None, dev_i32(wa.row_ke), wa.topk_blocks,
+                                        wa.block_size, oa, wa.row_repeat, workspace=wsa)
+        with torch.cuda.stream(sb):
+            dsa.select_candidate_blocks(xb, None, dev_i32(wb.row_ke), wb.topk_blocks,
+                                        wb.block_size, ob, wb.row_repeat, workspace=wsb)
+        outs_a.append(oa)
+        outs_b.append(ob)
+    torch.cuda.synchronize()
+    for oa, ob in zip(outs_a, outs_b):
+        assert np.array_equal(oa.cpu().numpy(), exp_a)
+        assert np.array_equal(ob.cpu().numpy(), exp_b)
+
+
+def test_large_k_and_full_sort():
+    rng = np.random.default_rng(3)
+    for k, width, B in ((4096, 40000, 8), (300, 20000, 64), (2000, 2000, 1)):
+        x = np.round(rng.standard_normal((6, width)).astype(np.float32) * 4) / 4
+        ke = rng.integers(0, width + 1, size=6).astype(np.int32)
+        w = workloads.Workload(f"k{k}", x, None, ke, B, k, 1)
+        for plan in (1, 2):
+            got, sc = gpu_select(w, plan, 7)
+            exp_out, exp_sc = oracle_select(w)
+            assert_same(got, sc, exp_out, exp_sc, f"k={k} plan {plan}")
+
+
+def test_all_equal_scores_take_lowest_ids():
+    x = np.full((3, 4096), 1.5, np.float32)
+    ke = np.array([4096, 100, 4095], np.int32)
+    w = workloads.Workload("flat", x, None, ke, 64, 10, 1)
+    got, _ = gpu_select(w, 1)
+    assert got[0].tolist() == [63] + list(range(9))
+    assert got[1].tolist() == [1, 0] + [-1] * 8
+    exp_out, _ = oracle_select(w)
+    assert np.array_equal(got, exp_out)
