@@ -65,6 +65,10 @@ def oracle_select(w, rows=None):
 
 
 def assert_same(got_out, got_sc, exp_out, exp_sc, ctx=""):
+    if got_out.ndim == 2 and got_out.shape[1] == 0 and got_sc is not None:
+        # topk_blocks == 0 writes nothing at all, not even the optional scores
+        assert (got_sc == 777.0).all(), ctx
+        return
     if not np.array_equal(got_out, exp_out):
         bad = np.argwhere(got_out != exp_out)
         r = bad[0][0]
