@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of DSA candidate-block selection on one MI355X.
 
-A step is one call of dsa_select_candidate_blocks (the fused single-launch
-path: windowed block max, pin, top-k, ordered -1 padded store) over one batch
-of the chosen synthetic workload, with its inputs already resident in HBM.
+A step is one call of dsa_select_candidate_blocks (windowed block max, pin,
+top-k, ordered -1 padded store; one launch, or two under the split plan) over
+one batch of the chosen synthetic workload, with its inputs already resident
+in HBM.
 The default workload is the decode batch (64 rows x 32768 columns, block 64,
 top-32, row_repeat 2).
 
@@ -49,8 +50,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
                     help="workload (1 tiny, 2 decode, 3 prefill, 4 long-context decode, 5 large prefill)")
-    ap.add_argument("--plan", type=int, default=0, choices=[0, 1, 2])
-    ap.add_argument("--chunk-blocks", type=int, default=0)
+    ap.add_argument("--plan", type=int, default=0, choices=[0, 1, 2, 3])
+    ap.add_argument("--plan-arg", type=int, default=0,
+                    help="plan 1: waves per workgroup; plan 2: blocks per chunk (0: automatic)")
     ap.add_argument("--rotate-bytes", type=float, default=2.0, help="GiB of input copies to rotate over")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget (0: skip)")
     ap.add_argument("--eager", action="store_true", help="launch every step from Python, no graph")
@@ -136,7 +138,7 @@ def main():
     nb = -(-w.width // w.block_size)
     plan, cb = dsa.select_plan(w.rows, w.width, w.block_size, w.topk_blocks)
     if args.plan:
-        plan, cb = args.plan, args.chunk_blocks
+        plan, cb = args.plan, args.plan_arg
     L = dsa.lib()
 
     ks = None if w.row_ks is None else torch.from_numpy(w.row_ks).to(dev)
@@ -154,7 +156,7 @@ def main():
 
     # parity once, before timing
     dsa.select_candidate_blocks(xs[0], ks, ke, w.topk_blocks, w.block_size, out, w.row_repeat,
-                                workspace=ws, plan=plan, chunk_blocks=cb)
+                                workspace=ws, plan=plan, plan_arg=cb)
     got = out.cpu().numpy()
     parity = None
     if not args.profile or w.rows <= 128:
@@ -246,7 +248,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "rows": w.rows, "width": w.width,
                    "block_size": w.block_size, "topk_blocks": w.topk_blocks,
-                   "row_repeat": w.row_repeat, "plan": plan, "chunk_blocks": cb,
+                   "row_repeat": w.row_repeat, "plan": plan, "plan_arg": cb,
                    "input_copies": copies, "graph": use_graph,
                    "logits_sha256": workloads.sha256(w.logits)[:16]},
         "rows_per_s": round(w.rows / (ms * 1e-3), 1),
@@ -255,7 +257,9 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_for(w.name, plan),
                      "algorithmic_bytes_per_launch": alg, "in_window_bytes": win,
-                     "kernel": "select_split_kernel" if plan == 2 else "select_rows_kernel"},
+                     "timed": "whole step (both kernels under the split plan)",
+                     "kernel": {1: "select_group_rows_kernel", 2: "stream_keys_kernel",
+                                3: "select_wave_rows_kernel"}[plan]},
     }
 
     if not args.profile:

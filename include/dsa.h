@@ -83,40 +83,42 @@ dsa_status_t dsa_block_scores(const float* logits, int64_t rows, int64_t width,
                               int64_t ld_scores, hipStream_t stream);
 
 /*
- * Bytes of device workspace dsa_select_candidate_blocks needs for this shape:
- * one uint32 arrival counter per row (rounded up to 256 bytes) plus one
- * uint32 score key per row and block.  Pure host arithmetic; returns 0 for
- * invalid or empty shapes.
+ * Bytes of device workspace the split plan of dsa_select_candidate_blocks
+ * needs for this shape (one uint32 score key per row and block); enough for
+ * every plan.  Pure host arithmetic; returns 0 for invalid or empty shapes.
  */
 size_t dsa_select_workspace_bytes(int64_t rows, int64_t width, int32_t block_size,
                                   int32_t topk_blocks);
 
 /*
- * Candidate-block selection, fused: one HBM pass over the in-window logits,
- * block scores in LDS, pin, top-k by radix select, ordered -1 padded store
- * (page: select_candidate_blocks, non-DCP branch; the tie order, score
- * descending then block id ascending, is this library's rule).
+ * Candidate-block selection: one HBM pass over the in-window logits, block
+ * scores kept as order-preserving keys (in LDS; in the workspace under the
+ * split plan), pin, top-k, ordered -1 padded store (page:
+ * select_candidate_blocks, non-DCP branch; the tie order, score descending
+ * then block id ascending, is this library's rule).
  *
  *   out         int32 [rows, ld_out], ld_out >= topk_blocks; columns
  *               [0, topk_blocks) of every row are written.
  *   scores_out  nullable fp32 [rows, ld_scores], ld_scores >= nblocks: the
  *               pinned block scores, for checking; ld_scores is ignored when
  *               scores_out is NULL.
- *   workspace   device memory of at least dsa_select_workspace_bytes(...)
- *               bytes, 4-byte aligned.  Zero it once before its first use
- *               (e.g. hipMemsetAsync); every call leaves it zeroed again.
- *               Calls that may run concurrently need separate workspaces.
+ *   workspace   device scratch for the split plan (few long rows): at least
+ *               dsa_select_workspace_bytes(...) bytes, 4-byte aligned, no
+ *               initialisation needed.  Other plans do not touch it and it
+ *               may then be NULL (dsa_select_plan tells the plan).  Calls
+ *               that may run concurrently need separate workspaces.
  *
  * rows == 0 or topk_blocks == 0: DSA_OK, nothing written.
- * width == 0: out[r][j] = -1 for j < topk_blocks (page: 'if not width:
- *   out.fill_(-1)'); logits/row_ke may then be NULL.
+ * width == 0: out[r][j] = -1 for j < topk_blocks (page: the early exit of
+ *   _select_candidate_blocks_impl for an empty width); logits/row_ke may
+ *   then be NULL.
  * Invalid: negative sizes, block_size < 1, row_repeat < 1, topk_blocks < 0,
  *   ld_logits < width, ld_out < topk_blocks, ld_scores < nblocks when
  *   scores_out is given, null logits/row_ke/out when there is work,
  *   misaligned pointers.
- * Unsupported: 4*nblocks + 8*min(topk_blocks, nblocks) + 1120 > 65536 (the
- *   row's block scores and the selected set must fit in LDS), or more than
- *   2^31 - 1 rows.
+ * Unsupported: 4 * (roundup4(nblocks) + roundup4(max(256, 2*kcap))) > 65536
+ *   with kcap = max(1, min(topk_blocks, nblocks)) (a row's block scores and
+ *   select scratch must fit in LDS), or more than 2^31 - 1 rows.
  */
 dsa_status_t dsa_select_candidate_blocks(const float* logits, int64_t rows, int64_t width,
                                          int64_t ld_logits, const int32_t* row_ks,
@@ -130,21 +132,27 @@ dsa_status_t dsa_select_candidate_blocks(const float* logits, int64_t rows, int6
  * dsa_select_candidate_blocks with an explicit launch plan, for tests and
  * tuning.  Results are identical for every plan.
  *   plan          0: automatic (what dsa_select_candidate_blocks uses);
- *                 1: one workgroup per row;
- *                 2: split rows into chunks of `chunk_blocks` blocks, the
- *                    last chunk of a row to finish runs the select.
- *   chunk_blocks  plan 2 only: blocks per chunk, >= 1 (0: automatic).
+ *                 1: one workgroup per row (its waves stream the row, one
+ *                    wave selects);
+ *                 2: split: a first kernel streams chunks of `plan_arg`
+ *                    blocks of every row on many CUs into the workspace, a
+ *                    second kernel selects, one wave per row;
+ *                 3: one wave per row (stream and select), several rows per
+ *                    workgroup.
+ *   plan_arg      plan 1: waves per workgroup, 1..16 (0: 4);
+ *                 plan 2: blocks per chunk, >= 1 (0: automatic);
+ *                 plan 3: float4 loads in flight per lane, 8 or 16 (0: 8).
  */
 dsa_status_t dsa_select_candidate_blocks_plan(
     const float* logits, int64_t rows, int64_t width, int64_t ld_logits,
     const int32_t* row_ks, const int32_t* row_ke, int32_t topk_blocks, int32_t block_size,
     int32_t row_repeat, int32_t* out, int64_t ld_out, float* scores_out, int64_t ld_scores,
-    void* workspace, size_t workspace_bytes, int32_t plan, int32_t chunk_blocks,
+    void* workspace, size_t workspace_bytes, int32_t plan, int32_t plan_arg,
     hipStream_t stream);
 
-/* The automatic plan for a shape: *plan = 1 or 2, *chunk_blocks (plan 2). */
+/* The automatic plan for a shape: *plan = 1, 2 or 3 and its *plan_arg. */
 dsa_status_t dsa_select_plan(int64_t rows, int64_t width, int32_t block_size,
-                             int32_t topk_blocks, int32_t* plan, int32_t* chunk_blocks);
+                             int32_t topk_blocks, int32_t* plan, int32_t* plan_arg);
 
 /* Static string naming a status code ("DSA_OK", ...); "unknown" otherwise. */
 const char* dsa_status_string(dsa_status_t status);

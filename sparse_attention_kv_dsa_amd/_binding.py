@@ -116,15 +116,16 @@ def select_plan(rows: int, width: int, block_size: int, topk_blocks: int) -> tup
 
 
 class Workspace:
-    """A zeroed device workspace for dsa_select_candidate_blocks (one per stream)."""
+    """Device scratch for the split plan of dsa_select_candidate_blocks
+    (no initialisation needed; one per stream that may run concurrently)."""
 
     def __init__(self, device, nbytes: int = 0):
         self.device = torch.device(device)
-        self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
 
     def ensure(self, nbytes: int) -> "Workspace":
         if nbytes > self.buf.numel():
-            self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         return self
 
 
@@ -163,13 +164,14 @@ def select_candidate_blocks(logits: torch.Tensor, row_ks: torch.Tensor | None,
                             out: torch.Tensor, row_repeat: int = 1, *,
                             scores_out: torch.Tensor | None = None,
                             workspace: Workspace | None = None,
-                            plan: int = 0, chunk_blocks: int = 0) -> None:
+                            plan: int = 0, plan_arg: int = 0) -> None:
     """Fill int32 ``out[rows, >=topk_blocks]`` with the selected block ids, -1 padded.
 
     Mirrors ``select_candidate_blocks(logits, row_ks, row_ke, topk_blocks,
     block_size, out, row_repeat)`` of the vLLM-fork candidate_blocks.py page
-    (non-DCP branch).  ``plan``/``chunk_blocks`` pick a launch plan (0 =
-    automatic); every plan gives identical results.
+    (non-DCP branch).  ``plan``/``plan_arg`` pick a launch plan (0 =
+    automatic, see dsa_select_candidate_blocks_plan); every plan gives
+    identical results.
     """
     ld = _check_logits(logits)
     rows, width = logits.shape
@@ -194,5 +196,5 @@ def select_candidate_blocks(logits: torch.Tensor, row_ks: torch.Tensor | None,
     code = lib().dsa_select_candidate_blocks_plan(
         _ptr(logits), rows, width, ld, _ptr(ks), _ptr(ke), topk_blocks, block_size, row_repeat,
         _ptr(out), _ld(out), _ptr(scores_out), ld_scores, workspace.buf.data_ptr(),
-        workspace.buf.numel(), plan, chunk_blocks, stream)
+        workspace.buf.numel(), plan, plan_arg, stream)
     _raise(code, "dsa_select_candidate_blocks")

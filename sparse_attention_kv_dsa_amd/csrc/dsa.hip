@@ -17,12 +17,20 @@
 //     16-lane row, ds_swizzle across rows and a bpermute across halves.
 //   * Scores are kept as order-preserving uint32 keys (unsigned order ==
 //     float order, canonical NaN on top), in LDS for the select.
-//   * Top-k: 8-bit-digit radix select in LDS finds the k-th largest rank key,
-//     the candidates are compacted in block-id order (so ties resolve to the
-//     lowest ids), and at most k-1 of them are ordered by counting rank.
-//   * Few long rows (decode): rows are split into chunks that run on many
-//     CUs; the last chunk of a row to finish (agent-scope counter) gathers
-//     the row's keys and runs the select, so a call is still one launch.
+//   * Top-k runs in one wave with no barrier: the row's rank keys sit in
+//     registers, an 8-bit-digit radix select (LDS histogram per pass, lane
+//     prefix scan, early exit when a whole bucket is taken) finds the k-th
+//     largest, candidates are compacted in block-id order with ballot/mbcnt
+//     (so ties resolve to the lowest ids), and the ones above the threshold
+//     are ordered by counting rank.
+//   * Launch plans: short rows take one wave per row (four rows per
+//     workgroup, no barrier at all); long rows take a workgroup whose four
+//     waves stream the row and hand the keys to one selecting wave; few long
+//     rows (decode) are split in chunks over many CUs by a streaming kernel
+//     that writes the block keys, and a second kernel selects.  Cross-CU
+//     hand-off inside one kernel would need agent-scope fences, which on
+//     this chip write back and invalidate a whole XCD's L2 each; the kernel
+//     boundary is the cheaper synchronisation.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,11 +42,6 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = 8;
 
-// LDS words before the per-row key array: radix histogram, wave totals, misc.
-constexpr int kHistWords = 256;
-constexpr int kWaveWords = 8;
-constexpr int kMiscWords = 16;
-constexpr int kHeadWords = kHistWords + kWaveWords + kMiscWords;  // 280 words = 1120 B
 constexpr size_t kLdsLimit = 65536;
 constexpr int64_t kMaxGrid = 1 << 20;
 
@@ -107,14 +110,16 @@ struct Params {
   const int32_t* ke;
   int32_t B, R, pin, k;
   int32_t nblocks, chunk_blocks, nchunks;
-  int32_t vec_ok;  // width % 4 == 0: float4 loads never cross the row's end
+  int32_t vec_ok;      // width % 4 == 0: float4 loads never cross the row's end
+  int32_t kcap;        // max(1, min(k, nblocks)): selected-set capacity
+  int32_t keys_words;  // LDS words for one row's keys (nblocks rounded up to 4)
+  int32_t wave_words;  // LDS words of one row's select state (keys + scratch)
   int32_t* out;
   int64_t ld_out;
   float* scores;  // block-scores output, or the optional write-back
   int64_t ld_scores;
-  uint32_t* ws_cnt;   // split select: one arrival counter per row
-  uint32_t* ws_keys;  // split select: [rows, nblocks] score keys
-  int64_t items;      // work items (rows * chunks)
+  uint32_t* ws_keys;  // split plan: [rows, nblocks] score keys
+  int64_t items;      // work items of the launch
 };
 
 // Per-row geometry derived from the bounds (all in 64-bit: bounds are
@@ -150,19 +155,37 @@ __device__ __forceinline__ RowGeom row_geom(const Params& p, int64_t r, bool pin
   return g;
 }
 
+// Orders this wave's LDS accesses (a wave's LDS operations complete in
+// issue order; this keeps the compiler from moving them across).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// This wave's index in the workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
 // Streams blocks [b0, b1) (b1 <= nvb) of a row on the vector path: s >= 0,
 // (row + s) 16-byte aligned and width % 4 == 0, so every float4 that holds an
-// in-window column lies inside the row.  B = 4*G.  Calls emit(b, max) once per
+// in-window column lies inside the row.  B = 4*G.  The chunk's 1 KiB tiles
+// are dealt to `nw` waves; this is wave `wv`.  Calls emit(b, max) once per
 // block, from one lane of the block.
 //
 // The loads are branch-free: a lane past the chunk's last unit re-reads that
-// unit (same cache line) and masks it, so all kUnroll loads of a lane issue
-// back to back.
-template <int G, class Emit>
-__device__ __forceinline__ void stream_vec(const RowGeom& g, int32_t b0, int32_t b1,
-                                           Emit& emit) {
+// unit (same cache line) and masks it, so all U loads of a lane issue back to
+// back.
+template <int G, int U, class Emit>
+__device__ __forceinline__ void stream_vec(const RowGeom& g, int32_t b0, int32_t b1, int wv,
+                                           int nw, const Emit& emit) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const float4* base = reinterpret_cast<const float4*>(g.row + g.s);
   const int32_t span = (int32_t)(g.hi - g.s);        // in-window columns from s
   const int32_t nu_row = (span + 3) >> 2;            // units holding one of them
@@ -170,16 +193,19 @@ __device__ __forceinline__ void stream_vec(const RowGeom& g, int32_t b0, int32_t
   const int32_t ue = b1 * G < nu_row ? b1 * G : nu_row;
   const int32_t ntiles = (ue - ub + 63) >> 6;
   const float ninf = -__builtin_inff();
-  for (int32_t t0 = wave; t0 < ntiles; t0 += kWaves * kUnroll) {
-    float4 v[kUnroll];
+  const char* cbase = reinterpret_cast<const char*>(base);
+  for (int32_t t0 = wv; t0 < ntiles; t0 += nw * U) {
+    float4 v[U];
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      const int32_t u = ub + ((t0 + j * kWaves) << 6) + lane;
-      v[j] = base[u < ue ? u : ue - 1];
+    for (int j = 0; j < U; ++j) {
+      // uniform base + 32-bit byte offset: the scalar-base form of the load
+      const int32_t u = ub + ((t0 + j * nw) << 6) + lane;
+      const uint32_t off = (uint32_t)(u < ue ? u : ue - 1) << 4;
+      v[j] = *reinterpret_cast<const float4*>(cbase + off);
     }
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      const int32_t t = t0 + j * kWaves;
+    for (int j = 0; j < U; ++j) {
+      const int32_t t = t0 + j * nw;
       const int32_t u = ub + (t << 6) + lane;
       const int32_t lim = u < ue ? span - 4 * u : 0;  // valid columns in this unit
       const float x = lim > 0 ? v[j].x : ninf;
@@ -199,19 +225,18 @@ __device__ __forceinline__ void stream_vec(const RowGeom& g, int32_t b0, int32_t
 // Any block size and alignment: gl = largest power of two <= min(B, 64)
 // lanes share a block, each striding over the block's in-window columns with
 // scalar loads, four in flight; a masked slot re-reads the block's first
-// in-window column.
+// in-window column.  Blocks are dealt to `nw` waves; this is wave `wv`.
 template <class Emit>
 __device__ __forceinline__ void stream_scalar(const RowGeom& g, int32_t B, int32_t b0,
-                                              int32_t b1, Emit& emit) {
+                                              int32_t b1, int wv, int nw, const Emit& emit) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   int gl = 1;
   while (gl * 2 <= B && gl < 64) gl *= 2;
   const int per_wave = 64 / gl;
   const int sub = lane & (gl - 1);
   const float ninf = -__builtin_inff();
-  for (int64_t bb = (int64_t)b0 + (int64_t)wave * per_wave; bb < b1;
-       bb += (int64_t)kWaves * per_wave) {
+  for (int64_t bb = (int64_t)b0 + (int64_t)wv * per_wave; bb < b1;
+       bb += (int64_t)nw * per_wave) {
     const int64_t b = bb + lane / gl;
     const int64_t cs = g.s + b * B;  // first column of block b
     const int64_t lo = b < b1 ? (cs > g.lo ? cs : g.lo) : 0;
@@ -232,25 +257,20 @@ __device__ __forceinline__ void stream_scalar(const RowGeom& g, int32_t B, int32
   }
 }
 
-template <int G, class Emit>
+template <int G, int U, class Emit>
 __device__ __forceinline__ void stream_blocks(const Params& p, const RowGeom& g, int32_t b0,
-                                              int32_t b1, Emit& emit) {
+                                              int32_t b1, int wv, int nw, const Emit& emit) {
   if (b1 <= b0) return;
   if constexpr (G > 0) {
     if (p.vec_ok && g.s >= 0 && ((reinterpret_cast<uintptr_t>(g.row + g.s) & 15u) == 0)) {
-      stream_vec<G>(g, b0, b1, emit);
+      stream_vec<G, U>(g, b0, b1, wv, nw, emit);
       return;
     }
   }
-  stream_scalar(g, p.B, b0, b1, emit);
+  stream_scalar(g, p.B, b0, b1, wv, nw, emit);
 }
 
-struct EmitKeyLds {
-  uint32_t* keys;
-  __device__ void operator()(int32_t b, float m) const { keys[b] = order_key(m); }
-};
-
-struct EmitKeyGlobal {
+struct EmitKey {  // LDS or HBM key array of one row
   uint32_t* keys;
   __device__ void operator()(int32_t b, float m) const { keys[b] = order_key(m); }
 };
@@ -265,215 +285,283 @@ struct EmitScore {
 
 // ---------------------------------------------------------------- select --
 
-__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* wave_tot) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Top-k over the score keys keys[0, nsel) of one row, by one wave.  KPL > 0
+// holds KPL rank keys per lane in registers (nsel <= 64*KPL); KPL == 0 reads
+// them from LDS on every pass.  Key i sits in lane i % 64, slot i / 64, so a
+// ballot over one slot lists ids in ascending order.  `scratch` is this
+// wave's LDS scratch: a 256-bin histogram, later the selected set
+// (max(256, 2*kcap) words, 16-byte aligned).
+template <int KPL>
+__device__ void select_wave(const uint32_t* keys, int32_t nsel, int32_t k, int32_t kcap,
+                            int32_t* out_row, uint32_t* scratch) {
+  const int lane = threadIdx.x & 63;
+  const int32_t nj = KPL > 0 ? KPL : (nsel + 63) >> 6;
+  uint32_t kv[KPL > 0 ? KPL : 1];
+  if constexpr (KPL > 0) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  if (lane == 0) wave_tot[wave] = v;
-  __syncthreads();
-  uint32_t t = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) t += wave_tot[w];
-  __syncthreads();
-  return t;
-}
-
-// Exclusive prefix sum over threads in thread order.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tot) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t y = __shfl_up(x, off);
-    if (lane >= off) x += y;
+    for (int j = 0; j < KPL; ++j) {
+      const int32_t i = j * 64 + lane;
+      kv[j] = i < nsel ? rank_key(keys[i]) : 0u;
+    }
   }
-  if (lane == 63) wave_tot[wave] = x;
-  __syncthreads();
-  uint32_t before = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) before += (w < wave) ? wave_tot[w] : 0u;
-  __syncthreads();
-  return before + x - v;
-}
+  auto key_at = [&](int32_t j) -> uint32_t {
+    if constexpr (KPL > 0) {
+      return kv[j];
+    } else {
+      const int32_t i = j * 64 + lane;
+      return i < nsel ? rank_key(keys[i]) : 0u;
+    }
+  };
 
-// Top-k over the score keys keys[0, nsel) of one row (all threads of the
-// workgroup call it).  Overwrites keys with rank keys.  Writes out_row[0, k).
-__device__ void select_topk(uint32_t* smem, uint32_t* keys, int32_t nsel, int32_t k,
-                            int32_t* out_row) {
-  uint32_t* hist = smem;
-  uint32_t* wave_tot = smem + kHistWords;
-  uint32_t* misc = wave_tot + kWaveWords;
-  uint32_t* sel_key = keys + nsel;
-  const int tid = threadIdx.x;
-
-  uint32_t cnt = 0;
-  for (int32_t i = tid; i < nsel; i += kThreads) {
-    const uint32_t rk = rank_key(keys[i]);
-    keys[i] = rk;
-    cnt += rk != 0u;
-  }
-  const uint32_t nvalid = block_sum(cnt, wave_tot);
+  uint32_t nvalid = 0;
+  for (int32_t j = 0; j < nj; ++j) nvalid += (uint32_t)__popcll(__ballot(key_at(j) != 0u));
   const int32_t keff = (uint32_t)k < nvalid ? k : (int32_t)nvalid;
 
-  // Threshold: candidates are rank keys >= tgt, plus the first need_eq keys
-  // equal to teq in block-id order.
-  uint32_t tgt = 1u, teq = 0u;
+  // The selection: every key >= tg, then the first need_eq keys equal to T
+  // in id order (need_eq > 0 only when ties at T straddle the k-th place).
+  uint32_t tg = 1u, T = 0u;
   int32_t need_eq = 0;
   if (keff > 0 && (uint32_t)keff < nvalid) {
-    uint32_t prefix = 0, remaining = (uint32_t)keff;
-    bool whole_bucket = false;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      hist[tid] = 0u;  // kThreads == 256 bins
-      __syncthreads();
-      const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
-      for (int32_t i = tid; i < nsel; i += kThreads) {
-        const uint32_t rk = keys[i];
-        if (rk != 0u && (rk & hmask) == prefix) atomicAdd(&hist[(rk >> shift) & 255u], 1u);
+    if constexpr (KPL >= 1 && KPL <= 4) {
+      // Few keys: bitwise binary search on the threshold, registers only.
+      // T ends as the largest value with #(key >= T) >= keff; if some probe
+      // has exactly keff keys at or above it, those keys are the selection.
+      bool exact = false;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        uint32_t cnt = 0;
+        for (int32_t j = 0; j < nj; ++j) cnt += (uint32_t)__popcll(__ballot(key_at(j) >= cand));
+        if (cnt >= (uint32_t)keff) {
+          T = cand;
+          if (cnt == (uint32_t)keff) {
+            exact = true;
+            break;
+          }
+        }
       }
-      __syncthreads();
-      // Thread t looks at digit 255 - t: the exclusive scan counts the keys
-      // whose digit is larger.
-      const uint32_t c = hist[255 - tid];
-      const uint32_t above = block_exclusive_scan(c, wave_tot);
-      if (above < remaining && above + c >= remaining) {
-        misc[0] = 255u - tid;
-        misc[1] = remaining - above;
-        misc[2] = c;
+      if (exact) {
+        tg = T;
+      } else {
+        uint32_t above = 0;
+        for (int32_t j = 0; j < nj; ++j) above += (uint32_t)__popcll(__ballot(key_at(j) > T));
+        tg = T + 1u;
+        need_eq = keff - (int32_t)above;
       }
-      __syncthreads();
-      const uint32_t d = misc[0], rem = misc[1], cb = misc[2];
-      __syncthreads();
-      prefix |= d << shift;
-      if (rem == cb) {  // the whole bucket is taken: every key >= prefix
-        whole_bucket = true;
-        break;
-      }
-      remaining = rem;
-    }
-    if (whole_bucket) {
-      tgt = prefix;
     } else {
-      tgt = prefix + 1u;
-      teq = prefix;
-      need_eq = (int32_t)remaining;
+      // Radix select, 8-bit digits from the top: `prefix` holds the digits
+      // fixed so far, `remaining` how many keys are still needed among the
+      // keys that match it (all keys above it are already in).  Ends with
+      // either a whole bucket taken (the selection is every key >= tg) or the
+      // exact keff-th largest key T (keys > T, then the first need_eq keys
+      // equal to T).
+      uint32_t* hist = scratch;
+      uint32_t prefix = 0u, remaining = (uint32_t)keff;
+      bool whole = false;
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+        wave_sync();
+        const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+        for (int32_t j = 0; j < nj; ++j) {
+          const uint32_t kj = key_at(j);
+          if (kj != 0u && (kj & hmask) == prefix) atomicAdd(&hist[(kj >> shift) & 255u], 1u);
+        }
+        wave_sync();
+        // lane l holds bins 255-4l (q = 0) down to 252-4l (q = 3); `above` is
+        // the number of matching keys in higher bins (lanes before this one)
+        const uint4 h = reinterpret_cast<const uint4*>(hist)[63 - lane];
+        const uint32_t tot = h.x + h.y + h.z + h.w;
+        uint32_t inc = tot;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t y = __shfl_up(inc, off);
+          if (lane >= off) inc += y;
+        }
+        const uint32_t a0 = inc - tot, a1 = a0 + h.w, a2 = a1 + h.z, a3 = a2 + h.y;
+        const bool h0 = a0 < remaining && remaining <= a1;
+        const bool h1 = a1 < remaining && remaining <= a2;
+        const bool h2 = a2 < remaining && remaining <= a3;
+        const bool h3 = a3 < remaining && remaining <= a3 + h.x;
+        const uint64_t hit = __ballot(h0 || h1 || h2 || h3);
+        const int src = (int)__builtin_ctzll(hit);  // exactly one lane holds the bucket
+        const uint32_t q = h0 ? 0u : (h1 ? 1u : (h2 ? 2u : 3u));
+        const uint32_t aq = h0 ? a0 : (h1 ? a1 : (h2 ? a2 : a3));
+        const uint32_t cq = h0 ? h.w : (h1 ? h.z : (h2 ? h.y : h.x));
+        const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)(255u - 4u * lane - q), src);
+        const uint32_t rem = (uint32_t)__builtin_amdgcn_readlane((int)(remaining - aq), src);
+        const uint32_t cb = (uint32_t)__builtin_amdgcn_readlane((int)cq, src);
+        prefix |= d << shift;
+        wave_sync();
+        if (rem == cb) {
+          whole = true;
+          break;
+        }
+        remaining = rem;
+      }
+      if (whole) {
+        tg = prefix;
+      } else {
+        T = prefix;
+        tg = prefix + 1u;
+        need_eq = (int32_t)remaining;
+      }
     }
   }
   const int32_t c_gt = keff - need_eq;
 
-  // Compaction in block-id order: thread t owns ids [t*m, t*m + m).
-  const int32_t m = (nsel + kThreads - 1) / kThreads;
-  const int32_t i0 = tid * m;
-  const int32_t i1 = i0 + m < nsel ? i0 + m : nsel;
-  uint32_t ngt = 0, neq = 0;
+  // Compaction in id order: keys >= tg into sel_*, the first need_eq keys
+  // equal to T straight to their final slots after them.
   if (keff > 0) {
-    for (int32_t i = i0; i < i1; ++i) {
-      const uint32_t rk = keys[i];
-      ngt += (rk >= tgt && rk != 0u);
-      neq += (need_eq > 0 && rk == teq);
-    }
-  }
-  const uint32_t packed = block_exclusive_scan((ngt << 16) | neq, wave_tot);
-  uint32_t off_gt = packed >> 16, off_eq = packed & 0xFFFFu;
-  if (keff > 0) {
-    uint32_t* sel_id = sel_key + (keff > 0 ? keff : 1);
-    for (int32_t i = i0; i < i1; ++i) {
-      const uint32_t rk = keys[i];
-      if (rk >= tgt && rk != 0u) {
-        sel_key[off_gt] = rk;
-        sel_id[off_gt] = (uint32_t)i;
-        ++off_gt;
-      } else if (need_eq > 0 && rk == teq) {
-        if (off_eq < (uint32_t)need_eq) out_row[c_gt + (int32_t)off_eq] = i;
-        ++off_eq;
+    uint32_t* sel_key = scratch;
+    uint32_t* sel_id = scratch + kcap;
+    uint32_t pos_gt = 0, pos_eq = 0;
+    for (int32_t j = 0; j < nj; ++j) {
+      const uint32_t kj = key_at(j);
+      const bool is_gt = kj >= tg && kj != 0u;
+      const bool is_eq = need_eq > 0 && kj == T;
+      const uint64_t m_gt = __ballot(is_gt);
+      const uint64_t m_eq = __ballot(is_eq);
+      if (is_gt) {
+        const uint32_t r = pos_gt + lanes_below(m_gt);
+        sel_key[r] = kj;
+        sel_id[r] = (uint32_t)(j * 64 + lane);
       }
+      if (is_eq) {
+        const uint32_t r = pos_eq + lanes_below(m_eq);
+        if (r < (uint32_t)need_eq) out_row[c_gt + (int32_t)r] = j * 64 + lane;
+      }
+      pos_gt += (uint32_t)__popcll(m_gt);
+      pos_eq += (uint32_t)__popcll(m_eq);
     }
-    __syncthreads();
-    // Order the keys above the threshold: rank = #larger + #equal with a
-    // smaller id (sel_* is in id order).
-    for (int32_t i = tid; i < c_gt; i += kThreads) {
-      const uint32_t ki = sel_key[i];
+    wave_sync();
+    // Order the outright selection: rank = #larger + #equal with a smaller id
+    // (sel_* is in id order).
+    if (c_gt <= 64) {
+      const uint32_t ki = lane < c_gt ? sel_key[lane] : 0u;
       int32_t r = 0;
       for (int32_t j = 0; j < c_gt; ++j) {
-        const uint32_t kj = sel_key[j];
-        r += (kj > ki) || (kj == ki && j < i);
+        const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)ki, j);
+        r += (kj > ki) || (kj == ki && j < lane);
       }
-      out_row[r] = (int32_t)sel_id[i];
+      if (lane < c_gt) out_row[r] = (int32_t)sel_id[lane];
+    } else {
+      for (int32_t i = lane; i < c_gt; i += 64) {
+        const uint32_t ki = sel_key[i];
+        int32_t r = 0;
+        for (int32_t j = 0; j < c_gt; ++j) {
+          const uint32_t kj = sel_key[j];
+          r += (kj > ki) || (kj == ki && j < i);
+        }
+        out_row[r] = (int32_t)sel_id[i];
+      }
     }
   }
-  for (int32_t j = keff + tid; j < k; j += kThreads) out_row[j] = -1;
+  for (int32_t j = keff + lane; j < k; j += 64) out_row[j] = -1;
 }
 
-// Shared tail of both select kernels: keys[0, nvb) hold the streamed block
-// keys; fill, pin, optional write-back, select.
-__device__ void finish_row(const Params& p, int64_t r, const RowGeom& g, uint32_t* smem,
-                           uint32_t* keys) {
-  for (int32_t b = g.nvb + (int32_t)threadIdx.x; b < g.nsel; b += kThreads) keys[b] = kKeyNegInf;
-  __syncthreads();
-  if (g.pin >= 0 && threadIdx.x == 0) keys[g.pin] = kKeyPosInf;
-  __syncthreads();
+// One wave finishes a row whose keys[0, nvb) hold the streamed block keys:
+// -inf up to nsel, pin, optional score write-back, select.  `wmem` is this
+// row's LDS state: keys (keys_words), then the select scratch.
+__device__ void finish_row_wave(const Params& p, int64_t r, const RowGeom& g, uint32_t* wmem) {
+  const int lane = threadIdx.x & 63;
+  uint32_t* keys = wmem;
+  for (int32_t b = g.nvb + lane; b < g.nsel; b += 64) keys[b] = kKeyNegInf;
+  wave_sync();
+  if (g.pin >= 0 && lane == 0) keys[g.pin] = kKeyPosInf;
+  wave_sync();
   if (p.scores) {
     float* srow = p.scores + r * p.ld_scores;
-    for (int32_t b = threadIdx.x; b < p.nblocks; b += kThreads)
+    for (int32_t b = lane; b < p.nblocks; b += 64)
       srow[b] = b < g.nsel ? key_value(keys[b]) : -__builtin_inff();
   }
-  select_topk(smem, keys, g.nsel, p.k, p.out + r * p.ld_out);
+  uint32_t* scratch = wmem + p.keys_words;
+  int32_t* out_row = p.out + r * p.ld_out;
+  const int32_t n = g.nsel;
+  if (n <= 64) select_wave<1>(keys, n, p.k, p.kcap, out_row, scratch);
+  else if (n <= 128) select_wave<2>(keys, n, p.k, p.kcap, out_row, scratch);
+  else if (n <= 256) select_wave<4>(keys, n, p.k, p.kcap, out_row, scratch);
+  else if (n <= 512) select_wave<8>(keys, n, p.k, p.kcap, out_row, scratch);
+  else if (n <= 1024) select_wave<16>(keys, n, p.k, p.kcap, out_row, scratch);
+  else select_wave<0>(keys, n, p.k, p.kcap, out_row, scratch);
 }
 
-// One workgroup per row: stream the row into LDS keys, then select.
-template <int G>
-__global__ void __launch_bounds__(kThreads) select_rows_kernel(Params p) {
+// Plan "wave": one wave per row, blockDim/64 rows per workgroup, no barrier.
+// U: float4 loads in flight per lane.
+template <int G, int U>
+__global__ void __launch_bounds__(kThreads) select_wave_rows_kernel(Params p) {
   extern __shared__ uint32_t smem[];
-  uint32_t* keys = smem + kHeadWords;
-  for (int64_t r = blockIdx.x; r < p.items; r += gridDim.x) {
+  const int wave = wave_index();
+  const int nw = blockDim.x >> 6;
+  uint32_t* wmem = smem + wave * p.wave_words;
+  for (int64_t r = (int64_t)blockIdx.x * nw + wave; r < p.items; r += (int64_t)gridDim.x * nw) {
     const RowGeom g = row_geom(p, r, true);
-    EmitKeyLds emit{keys};
-    stream_blocks<G>(p, g, 0, g.nvb, emit);
-    __syncthreads();
-    finish_row(p, r, g, smem, keys);
-    __syncthreads();
+    stream_blocks<G, U>(p, g, 0, g.nvb, 0, 1, EmitKey{wmem});
+    wave_sync();
+    finish_row_wave(p, r, g, wmem);
+    wave_sync();
   }
 }
 
-// Rows split in chunks of chunk_blocks blocks; item = r * nchunks + c.  Only
-// the chunks that hold in-window blocks (at least chunk 0) take part; the last
-// of them to arrive gathers the row's keys and selects.
+// Plan "group": all waves of a workgroup stream one row into LDS, wave 0
+// selects.
 template <int G>
-__global__ void __launch_bounds__(kThreads) select_split_kernel(Params p) {
+__global__ void __launch_bounds__(1024) select_group_rows_kernel(Params p) {
   extern __shared__ uint32_t smem[];
-  uint32_t* keys = smem + kHeadWords;
-  uint32_t* misc = smem + kHistWords + kWaveWords;
+  const int wave = wave_index();
+  const int nw = blockDim.x >> 6;
+  for (int64_t r = blockIdx.x; r < p.items; r += gridDim.x) {
+    const RowGeom g = row_geom(p, r, true);
+    stream_blocks<G, kUnroll>(p, g, 0, g.nvb, wave, nw, EmitKey{smem});
+    __syncthreads();
+    if (wave == 0) finish_row_wave(p, r, g, smem);
+    if (r + gridDim.x < p.items) __syncthreads();  // LDS is reused by the next row
+  }
+}
+
+// Plan "split", first kernel: item = r * nchunks + c streams blocks
+// [c*chunk_blocks, (c+1)*chunk_blocks) of row r (in-window part only) into
+// the HBM key matrix ws_keys[r, b].
+template <int G>
+__global__ void __launch_bounds__(kThreads) stream_keys_kernel(Params p) {
+  const int wave = wave_index();
+  const int nw = blockDim.x >> 6;
   for (int64_t item = blockIdx.x; item < p.items; item += gridDim.x) {
     const int64_t r = item / p.nchunks;
     const int32_t c = (int32_t)(item - r * p.nchunks);
     const RowGeom g = row_geom(p, r, true);
-    const int32_t nact = g.nvb > 0 ? (g.nvb + p.chunk_blocks - 1) / p.chunk_blocks : 1;
-    if (c >= nact) continue;  // uniform across the workgroup
     const int32_t b0 = c * p.chunk_blocks;
+    if (b0 >= g.nvb) continue;
     const int32_t b1 = b0 + p.chunk_blocks < g.nvb ? b0 + p.chunk_blocks : g.nvb;
-    uint32_t* wrow = p.ws_keys + r * p.nblocks;
-    EmitKeyGlobal emit{wrow};
-    stream_blocks<G>(p, g, b0, b1, emit);
-    // Release this chunk's keys at agent scope (the chunks of a row run on
-    // different XCDs, each with its own L2), then count the arrival.
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const uint32_t old = atomicAdd(p.ws_cnt + r, 1u);
-      const uint32_t last = old + 1u == (uint32_t)nact;
-      if (last) __hip_atomic_store(p.ws_cnt + r, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __threadfence();
-      misc[8] = last;
+    stream_blocks<G, kUnroll>(p, g, b0, b1, wave, nw, EmitKey{p.ws_keys + r * p.nblocks});
+  }
+}
+
+// Plan "split", second kernel: one wave per row reads the row's keys back
+// and selects.
+__global__ void __launch_bounds__(kThreads) select_keys_kernel(Params p) {
+  extern __shared__ uint32_t smem[];
+  const int wave = wave_index();
+  const int lane = threadIdx.x & 63;
+  const int nw = blockDim.x >> 6;
+  uint32_t* wmem = smem + wave * p.wave_words;
+  for (int64_t r = (int64_t)blockIdx.x * nw + wave; r < p.items; r += (int64_t)gridDim.x * nw) {
+    const RowGeom g = row_geom(p, r, true);
+    const uint32_t* src = p.ws_keys + r * p.nblocks;
+    for (int32_t b0 = 0; b0 < g.nvb; b0 += 64 * 16) {  // 16 loads in flight per lane
+      uint32_t v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int32_t b = b0 + j * 64 + lane;
+        v[j] = src[b < g.nvb ? b : g.nvb - 1];
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int32_t b = b0 + j * 64 + lane;
+        if (b < g.nvb) wmem[b] = v[j];
+      }
     }
-    __syncthreads();
-    const bool last = misc[8] != 0u;
-    __syncthreads();
-    if (!last) continue;
-    __threadfence();  // acquire: the other chunks' keys
-    for (int32_t b = threadIdx.x; b < g.nvb; b += kThreads)
-      keys[b] = __hip_atomic_load(wrow + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    finish_row(p, r, g, smem, keys);
-    __syncthreads();
+    wave_sync();
+    finish_row_wave(p, r, g, wmem);
+    wave_sync();
   }
 }
 
@@ -481,6 +569,8 @@ __global__ void __launch_bounds__(kThreads) select_split_kernel(Params p) {
 // [c*chunk_blocks, (c+1)*chunk_blocks) of row r, in-window or not.
 template <int G>
 __global__ void __launch_bounds__(kThreads) block_scores_kernel(Params p) {
+  const int wave = wave_index();
+  const int nw = blockDim.x >> 6;
   for (int64_t item = blockIdx.x; item < p.items; item += gridDim.x) {
     const int64_t r = item / p.nchunks;
     const int32_t c = (int32_t)(item - r * p.nchunks);
@@ -489,10 +579,9 @@ __global__ void __launch_bounds__(kThreads) block_scores_kernel(Params p) {
     const int32_t b1 = b0 + p.chunk_blocks < p.nblocks ? b0 + p.chunk_blocks : p.nblocks;
     float* srow = p.scores + r * p.ld_scores;
     const int32_t sb1 = b1 < g.nvb ? b1 : g.nvb;
-    EmitScore emit{srow, g.pin};
-    stream_blocks<G>(p, g, b0, sb1, emit);
+    stream_blocks<G, kUnroll>(p, g, b0, sb1, wave, nw, EmitScore{srow, g.pin});
     const int32_t f0 = b0 > g.nvb ? b0 : g.nvb;
-    for (int32_t b = f0 + (int32_t)threadIdx.x; b < b1; b += kThreads)
+    for (int32_t b = f0 + (int32_t)threadIdx.x; b < b1; b += (int32_t)blockDim.x)
       srow[b] = b == g.pin ? __builtin_inff() : -__builtin_inff();
   }
 }
@@ -532,15 +621,35 @@ int lanes_per_block(int32_t B) {
     }                                                                                 \
   }
 
-DSA_KERNEL_TABLE(select_rows_kernel)
-DSA_KERNEL_TABLE(select_split_kernel)
+#define DSA_WAVE_TABLE(U)                                                             \
+  void* select_wave_rows_u##U##_ptr(int g) {                                          \
+    switch (g) {                                                                      \
+      case 1: return reinterpret_cast<void*>(&select_wave_rows_kernel<1, U>);         \
+      case 2: return reinterpret_cast<void*>(&select_wave_rows_kernel<2, U>);         \
+      case 4: return reinterpret_cast<void*>(&select_wave_rows_kernel<4, U>);         \
+      case 8: return reinterpret_cast<void*>(&select_wave_rows_kernel<8, U>);         \
+      case 16: return reinterpret_cast<void*>(&select_wave_rows_kernel<16, U>);       \
+      case 32: return reinterpret_cast<void*>(&select_wave_rows_kernel<32, U>);       \
+      case 64: return reinterpret_cast<void*>(&select_wave_rows_kernel<64, U>);       \
+      default: return reinterpret_cast<void*>(&select_wave_rows_kernel<0, U>);        \
+    }                                                                                 \
+  }
+
+DSA_WAVE_TABLE(8)
+DSA_WAVE_TABLE(16)
+DSA_KERNEL_TABLE(select_group_rows_kernel)
+DSA_KERNEL_TABLE(stream_keys_kernel)
 DSA_KERNEL_TABLE(block_scores_kernel)
 
-dsa_status_t launch(void* fn, int64_t items, size_t lds, hipStream_t stream, Params& p) {
+// Launches `fn` over `items` work items with `threads` per workgroup and
+// `per_group` items per workgroup.
+dsa_status_t launch(void* fn, int64_t items, int threads, int per_group, size_t lds,
+                    hipStream_t stream, Params& p) {
   p.items = items;
-  const int64_t grid = items < kMaxGrid ? items : kMaxGrid;
+  int64_t grid = (items + per_group - 1) / per_group;
+  if (grid > kMaxGrid) grid = kMaxGrid;
   void* args[] = {&p};
-  hipError_t err = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), args, lds, stream);
+  hipError_t err = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(threads), args, lds, stream);
   if (err != hipSuccess) {
     (void)hipGetLastError();
     return DSA_ERR_HIP;
@@ -554,12 +663,23 @@ bool misaligned(const void* ptr, uintptr_t a) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-size_t counters_bytes(int64_t rows) { return (size_t)cdiv(rows * 4, 256) * 256; }
-
-size_t select_lds_bytes(int64_t nblocks, int32_t k) {
-  const int64_t kcap = k < nblocks ? k : nblocks;
-  return (size_t)(kHeadWords + nblocks + 2 * (kcap > 0 ? kcap : 1)) * 4;
+int64_t select_kcap(int64_t nblocks, int32_t k) {
+  const int64_t kc = k < nblocks ? k : nblocks;
+  return kc > 0 ? kc : 1;
 }
+
+// LDS words of one row's select state: keys, then a scratch that holds the
+// radix histogram (256 words) and later the selected keys and ids; a
+// multiple of 4 words.
+int64_t select_keys_words(int64_t nblocks) { return cdiv(nblocks, 4) * 4; }
+
+int64_t select_wave_words(int64_t nblocks, int32_t k) {
+  const int64_t sel = 2 * select_kcap(nblocks, k);
+  return select_keys_words(nblocks) + cdiv(sel > 256 ? sel : 256, 4) * 4;
+}
+
+// Plan ids (also the values of dsa_select_candidate_blocks_plan's `plan`).
+enum { kPlanGroup = 1, kPlanSplit = 2, kPlanWave = 3 };
 
 // Chunk size for split rows: aim at ~2048 workgroups in total, 2K-16K columns
 // each, and a multiple of the blocks one wave instruction covers.
@@ -597,23 +717,31 @@ size_t dsa_select_workspace_bytes(int64_t rows, int64_t width, int32_t block_siz
                                   int32_t topk_blocks) {
   if (rows <= 0 || width <= 0 || block_size < 1 || topk_blocks < 0) return 0;
   const int64_t nblocks = cdiv(width, block_size);
-  return counters_bytes(rows) + (size_t)rows * (size_t)nblocks * 4u;
+  return (size_t)rows * (size_t)nblocks * 4u;
 }
 
 dsa_status_t dsa_select_plan(int64_t rows, int64_t width, int32_t block_size,
-                             int32_t topk_blocks, int32_t* plan, int32_t* chunk_blocks) {
-  if (rows < 0 || width < 0 || block_size < 1 || topk_blocks < 0 || !plan || !chunk_blocks)
+                             int32_t topk_blocks, int32_t* plan, int32_t* plan_arg) {
+  if (rows < 0 || width < 0 || block_size < 1 || topk_blocks < 0 || !plan || !plan_arg)
     return DSA_ERR_INVALID_ARG;
   const int64_t nblocks = width > 0 ? cdiv(width, block_size) : 0;
   const int32_t cb = auto_chunk_blocks(rows, width, block_size);
   const int64_t nchunks = cdiv(nblocks, cb);
-  // Many rows fill the GPU one workgroup per row; few long rows are split.
+  *plan_arg = 0;
   if (rows >= 1024 || nchunks <= 1) {
-    *plan = 1;
-    *chunk_blocks = 0;
+    // Enough rows to fill the GPU one row at a time: short rows one wave
+    // each, long rows a whole workgroup each.
+    *plan = width <= 16384 ? kPlanWave : kPlanGroup;
+    if (*plan == kPlanGroup) *plan_arg = kWaves;
+  } else if (rows >= 64) {
+    // Decode batches: one CU per row with up to 16 waves streaming it, the
+    // select fused behind them (a single launch; measured faster than the
+    // split plan's two kernels down to 64 rows).
+    *plan = kPlanGroup;
+    *plan_arg = rows <= 256 ? 16 : (rows <= 512 ? 8 : kWaves);
   } else {
-    *plan = 2;
-    *chunk_blocks = cb;
+    *plan = kPlanSplit;
+    *plan_arg = cb;
   }
   return DSA_OK;
 }
@@ -654,18 +782,21 @@ dsa_status_t dsa_block_scores(const float* logits, int64_t rows, int64_t width,
   p.nchunks = (int32_t)cdiv(nblocks, cb);
   p.scores = scores;
   p.ld_scores = ld_scores;
-  return launch(block_scores_kernel_ptr(g), rows * p.nchunks, 0, stream, p);
+  return launch(block_scores_kernel_ptr(g), rows * p.nchunks, kThreads, 1, 0, stream, p);
 }
 
 dsa_status_t dsa_select_candidate_blocks_plan(
     const float* logits, int64_t rows, int64_t width, int64_t ld_logits,
     const int32_t* row_ks, const int32_t* row_ke, int32_t topk_blocks, int32_t block_size,
     int32_t row_repeat, int32_t* out, int64_t ld_out, float* scores_out, int64_t ld_scores,
-    void* workspace, size_t workspace_bytes, int32_t plan, int32_t chunk_blocks,
+    void* workspace, size_t workspace_bytes, int32_t plan, int32_t plan_arg,
     hipStream_t stream) {
   if (rows < 0 || width < 0 || block_size < 1 || row_repeat < 1 || topk_blocks < 0)
     return DSA_ERR_INVALID_ARG;
-  if (plan < 0 || plan > 2 || chunk_blocks < 0) return DSA_ERR_INVALID_ARG;
+  if (plan < 0 || plan > 3 || plan_arg < 0) return DSA_ERR_INVALID_ARG;
+  if (plan == kPlanGroup && plan_arg > 16) return DSA_ERR_INVALID_ARG;
+  if (plan == kPlanWave && plan_arg != 0 && plan_arg != 8 && plan_arg != 16)
+    return DSA_ERR_INVALID_ARG;
   if (ld_logits < width || ld_out < topk_blocks) return DSA_ERR_INVALID_ARG;
   const int64_t nblocks = cdiv(width, block_size);
   if (scores_out && ld_scores < nblocks) return DSA_ERR_INVALID_ARG;
@@ -683,18 +814,16 @@ dsa_status_t dsa_select_candidate_blocks_plan(
   if (!logits || !row_ke) return DSA_ERR_INVALID_ARG;
   if (misaligned(logits, 4) || (scores_out && misaligned(scores_out, 4)))
     return DSA_ERR_INVALID_ARG;
-  const size_t lds = select_lds_bytes(nblocks, topk_blocks);
-  if (lds > kLdsLimit) return DSA_ERR_UNSUPPORTED;
-  const size_t need = dsa_select_workspace_bytes(rows, width, block_size, topk_blocks);
-  if (!workspace || workspace_bytes < need || misaligned(workspace, 4)) return DSA_ERR_WORKSPACE;
+  const int64_t ww = select_wave_words(nblocks, topk_blocks);
+  if (ww * 4 > (int64_t)kLdsLimit) return DSA_ERR_UNSUPPORTED;
 
-  int32_t auto_plan = 1, auto_cb = 0;
-  dsa_select_plan(rows, width, block_size, topk_blocks, &auto_plan, &auto_cb);
-  if (plan == 0) {
-    plan = auto_plan;
-    chunk_blocks = auto_cb;
+  if (plan == 0) dsa_select_plan(rows, width, block_size, topk_blocks, &plan, &plan_arg);
+  if (plan == kPlanSplit) {
+    if (plan_arg == 0) plan_arg = auto_chunk_blocks(rows, width, block_size);
+    const size_t need = dsa_select_workspace_bytes(rows, width, block_size, topk_blocks);
+    if (!workspace || workspace_bytes < need || misaligned(workspace, 4))
+      return DSA_ERR_WORKSPACE;
   }
-  if (plan == 2 && chunk_blocks == 0) chunk_blocks = auto_chunk_blocks(rows, width, block_size);
 
   Params p = {};
   p.logits = logits;
@@ -709,22 +838,34 @@ dsa_status_t dsa_select_candidate_blocks_plan(
   p.k = topk_blocks;
   p.nblocks = (int32_t)nblocks;
   p.vec_ok = (width % 4) == 0 && width < ((int64_t)1 << 30);
+  p.kcap = (int32_t)select_kcap(nblocks, topk_blocks);
+  p.keys_words = (int32_t)select_keys_words(nblocks);
+  p.wave_words = (int32_t)ww;
   p.out = out;
   p.ld_out = ld_out;
   p.scores = scores_out;
   p.ld_scores = ld_scores;
-  p.ws_cnt = static_cast<uint32_t*>(workspace);
-  p.ws_keys = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + counters_bytes(rows));
+  p.ws_keys = static_cast<uint32_t*>(workspace);
   const int g = lanes_per_block(block_size);
-  if (plan == 1) {
-    p.chunk_blocks = p.nblocks;
-    p.nchunks = 1;
-    return launch(select_rows_kernel_ptr(g), rows, lds, stream, p);
+  // waves per workgroup for the one-wave-per-row kernels: as many row states
+  // as fit in LDS, up to four
+  int64_t nw = (int64_t)kLdsLimit / (ww * 4);
+  if (nw > kWaves) nw = kWaves;
+  const size_t wave_lds = (size_t)(nw * ww * 4);
+  if (plan == kPlanWave)
+    return launch(plan_arg == 16 ? select_wave_rows_u16_ptr(g) : select_wave_rows_u8_ptr(g), rows,
+                  64 * (int)nw, (int)nw, wave_lds, stream, p);
+  if (plan == kPlanGroup) {
+    const int waves = plan_arg > 0 ? plan_arg : kWaves;
+    return launch(select_group_rows_kernel_ptr(g), rows, 64 * waves, 1, (size_t)ww * 4, stream, p);
   }
-  p.chunk_blocks = chunk_blocks < p.nblocks ? chunk_blocks : p.nblocks;
+  p.chunk_blocks = plan_arg < p.nblocks ? plan_arg : p.nblocks;
   p.nchunks = (int32_t)cdiv(nblocks, p.chunk_blocks);
   if (rows * (int64_t)p.nchunks > (int64_t)INT32_MAX) return DSA_ERR_UNSUPPORTED;
-  return launch(select_split_kernel_ptr(g), rows * p.nchunks, lds, stream, p);
+  dsa_status_t st = launch(stream_keys_kernel_ptr(g), rows * p.nchunks, kThreads, 1, 0, stream, p);
+  if (st != DSA_OK) return st;
+  return launch(reinterpret_cast<void*>(&select_keys_kernel), rows, 64 * (int)nw, (int)nw,
+                wave_lds, stream, p);
 }
 
 dsa_status_t dsa_select_candidate_blocks(const float* logits, int64_t rows, int64_t width,

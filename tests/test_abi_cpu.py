@@ -51,9 +51,9 @@ def test_status_strings():
 
 def test_workspace_bytes():
     L = B.lib()
-    # 64 rows -> 256 B of counters; 64 x 512 keys
-    assert L.dsa_select_workspace_bytes(64, 32768, 64, 32) == 256 + 64 * 512 * 4
-    assert L.dsa_select_workspace_bytes(65, 100, 7, 3) == 512 + 65 * 15 * 4
+    # one uint32 key per row and block
+    assert L.dsa_select_workspace_bytes(64, 32768, 64, 32) == 64 * 512 * 4
+    assert L.dsa_select_workspace_bytes(65, 100, 7, 3) == 65 * 15 * 4
     assert L.dsa_select_workspace_bytes(0, 100, 7, 3) == 0
     assert L.dsa_select_workspace_bytes(5, 0, 7, 3) == 0
     assert L.dsa_select_workspace_bytes(5, 100, 0, 3) == 0
@@ -61,13 +61,14 @@ def test_workspace_bytes():
 
 
 def test_auto_plan():
-    assert B.select_plan(4096, 16384, 64, 32)[0] == 1      # many rows: a workgroup per row
-    assert B.select_plan(8192, 65536, 64, 64)[0] == 1
-    assert B.select_plan(8, 1000, 64, 4)[0] == 1           # one chunk per row anyway
-    p, cb = B.select_plan(64, 32768, 64, 32)               # few long rows: split
-    assert p == 2 and cb % 4 == 0 and cb >= 1
-    p, cb = B.select_plan(128, 131072, 128, 16)
-    assert p == 2 and cb % 2 == 0
+    assert B.select_plan(4096, 16384, 64, 32) == (3, 0)    # many short rows: a wave per row
+    assert B.select_plan(8192, 65536, 64, 64) == (1, 4)    # many long rows: a workgroup per row
+    assert B.select_plan(8, 1000, 64, 4) == (3, 0)         # one chunk per row anyway
+    assert B.select_plan(64, 32768, 64, 32) == (1, 16)     # decode: a 16-wave CU per row
+    assert B.select_plan(128, 131072, 128, 16) == (1, 16)
+    assert B.select_plan(600, 131072, 128, 16) == (1, 4)
+    p, cb = B.select_plan(16, 131072, 128, 16)             # very few long rows: split
+    assert p == 2 and cb % 2 == 0 and cb >= 1
 
 
 def _sel(**kw):
@@ -82,12 +83,16 @@ def _sel(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(rows=-1), 1), (dict(width=-1), 1), (dict(B=0), 1), (dict(R=0), 1), (dict(k=-1), 1),
-    (dict(ld=63), 1), (dict(ld_out=3), 1), (dict(plan=3), 1), (dict(plan=-1), 1), (dict(cb=-1), 1),
+    (dict(ld=63), 1), (dict(ld_out=3), 1), (dict(plan=4), 1), (dict(plan=-1), 1), (dict(cb=-1), 1),
+    (dict(plan=1, cb=17), 1), (dict(plan=3, cb=4), 1),
     (dict(scores=FAKE, ld_scores=7), 1),         # nblocks = 8
     (dict(out=None), 1), (dict(out=FAKE2 + 2), 1), (dict(logits=None), 1), (dict(ke=None), 1),
     (dict(logits=FAKE + 2), 1), (dict(scores=FAKE + 1, ld_scores=8), 1),
-    (dict(ws=None), 3), (dict(ws_bytes=100), 3), (dict(ws=FAKE + 2), 3),
+    (dict(ws=None, plan=2), 3), (dict(ws_bytes=100, plan=2), 3), (dict(ws=FAKE + 2, plan=2), 3),
+    (dict(ws=None, plan=2, cb=3), 3),
     (dict(width=1 << 20, ld=1 << 20, B=16, k=4096, ld_out=4096), 2),  # keys do not fit in LDS
+    (dict(width=16128 * 4 + 4, ld=1 << 16, B=4, k=3, ld_out=3), 2),   # 16132 + 256 words > 16384
+    (dict(width=16128 * 4, ld=1 << 16, B=4, k=3, ld_out=3, plan=2, ws=None), 3),  # 16128 + 256 fits
     (dict(rows=0), 0), (dict(k=0), 0), (dict(rows=0, logits=None, ke=None, out=None), 0),
 ])
 def test_select_rejects_on_host(kw, code):

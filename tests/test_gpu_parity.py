@@ -39,6 +39,11 @@ def dev_i32(a):
 
 
 def gpu_select(w, plan=0, cb=0, ld_pad=0, offset=0, with_scores=True, ld_out_pad=0):
+    """cb: the plan argument (plan 1: waves per workgroup, plan 2: blocks per chunk)."""
+    if plan == 1 and cb:
+        cb = 1 + (cb - 1) % 16
+    if plan == 3:
+        cb = 16 if cb % 2 else 8
     x = dev_logits(w.logits, ld_pad, offset)
     nb = -(-w.width // w.block_size)
     out_full = torch.full((w.rows, w.topk_blocks + ld_out_pad), 12345, dtype=torch.int32, device=DEV)
@@ -48,7 +53,7 @@ def gpu_select(w, plan=0, cb=0, ld_pad=0, offset=0, with_scores=True, ld_out_pad
         sc = torch.full((w.rows, max(nb, 1)), 777.0, dtype=torch.float32, device=DEV)[:, :nb]
     dsa.select_candidate_blocks(x, dev_i32(w.row_ks), dev_i32(w.row_ke), w.topk_blocks,
                                 w.block_size, out, w.row_repeat, scores_out=sc, plan=plan,
-                                chunk_blocks=cb)
+                                plan_arg=cb)
     torch.cuda.synchronize()
     if ld_out_pad:
         assert (out_full[:, w.topk_blocks:] == 12345).all(), "wrote past topk_blocks"
@@ -108,7 +113,7 @@ def _golden_workload(c):
                               c["topk"], c["row_repeat"])
 
 
-@pytest.mark.parametrize("plan,cb", [(1, 0), (2, 1), (2, 2)])
+@pytest.mark.parametrize("plan,cb", [(1, 0), (1, 1), (1, 16), (2, 1), (2, 2), (3, 0), (3, 1)])
 def test_hand_worked_rows(plan, cb):
     for c in _golden():
         w = _golden_workload(c)
@@ -118,7 +123,7 @@ def test_hand_worked_rows(plan, cb):
         assert_same(got, sc, exp_out, exp_sc, c["id"])
 
 
-@pytest.mark.parametrize("plan", [1, 2])
+@pytest.mark.parametrize("plan", [1, 2, 3])
 def test_random_tiny_cases(plan):
     """400 tiny cases: NaN, +-0, +-inf, ties, odd widths and block sizes,
     negative/overlong/empty windows, row_repeat 1-3, k 0-12."""
@@ -133,7 +138,7 @@ def test_random_tiny_cases(plan):
 MEDIUM_B = [1, 3, 4, 5, 8, 12, 16, 32, 64, 100, 128, 256, 512]
 
 
-@pytest.mark.parametrize("plan", [1, 2])
+@pytest.mark.parametrize("plan", [1, 2, 3])
 def test_random_medium_cases(plan):
     """Several tiles per row and ragged tails, aligned (vector) and unaligned
     (scalar) rows, both launch plans with assorted chunk sizes."""
@@ -207,10 +212,11 @@ def test_config_full(cfg):
     exp_out, exp_sc = oracle_select(w)
     got, sc = gpu_select(w)
     assert_same(got, sc, exp_out, exp_sc, w.name)
-    # the other plan gives the same bits
+    # the other plans give the same bits
     auto = dsa.select_plan(w.rows, w.width, w.block_size, w.topk_blocks)[0]
-    got2, sc2 = gpu_select(w, plan=3 - auto)
-    assert_same(got2, sc2, exp_out, exp_sc, w.name + " other plan")
+    for plan in {1, 2, 3} - {auto}:
+        got2, sc2 = gpu_select(w, plan=plan)
+        assert_same(got2, sc2, exp_out, exp_sc, f"{w.name} plan {plan}")
 
 
 def _check_properties(out, nblocks):
@@ -271,37 +277,35 @@ def test_errors_write_nothing():
     with pytest.raises(dsa.DsaError) as e:
         dsa.select_candidate_blocks(x, None, ke, 5, 8, out)   # ld_out < topk
     assert e.value.code == 1
-    big = torch.ones((1, 1 << 18), device=DEV)
-    with pytest.raises(dsa.DsaError) as e:                    # 65536 keys exceed LDS
+    big = torch.ones((1, 1 << 16), device=DEV)
+    with pytest.raises(dsa.DsaError) as e:                    # 16384 keys + scratch exceed LDS
         dsa.select_candidate_blocks(big, None, ke[:1], 4, 4, out[:1])
     assert e.value.code == 2
     ws = dsa.Workspace(DEV, 64)
     lib = dsa.lib()
-    code = lib.dsa_select_candidate_blocks(x.data_ptr(), 4, 64, 64, None, ke.data_ptr(), 4, 8, 1,
-                                           out.data_ptr(), 4, None, 0, ws.buf.data_ptr(), 64,
-                                           torch.cuda.current_stream().cuda_stream)
-    assert code == 3
+    code = lib.dsa_select_candidate_blocks_plan(x.data_ptr(), 4, 64, 64, None, ke.data_ptr(), 4, 8,
+                                                1, out.data_ptr(), 4, None, 0, ws.buf.data_ptr(),
+                                                64, 2, 0, torch.cuda.current_stream().cuda_stream)
+    assert code == 3   # the split plan needs 4 * 8 keys * 4 bytes
     torch.cuda.synchronize()
     assert (out == 7).all()
 
 
-def test_repeat_calls_bit_identical_and_workspace_restored():
+def test_repeat_calls_bit_identical():
     w = workloads.config(2)
     x = dev_logits(w.logits)
     ks, ke = dev_i32(w.row_ks), dev_i32(w.row_ke)
     ws = dsa.Workspace(DEV)
     first = None
-    for plan, cb in ((2, 0), (2, 4), (1, 0)):
+    for plan, cb in ((2, 0), (2, 4), (1, 0), (1, 16), (3, 0), (3, 16)):
         for _ in range(50):
             out = torch.empty((w.rows, w.topk_blocks), dtype=torch.int32, device=DEV)
             dsa.select_candidate_blocks(x, ks, ke, w.topk_blocks, w.block_size, out, w.row_repeat,
-                                        workspace=ws, plan=plan, chunk_blocks=cb)
+                                        workspace=ws, plan=plan, plan_arg=cb)
             o = out.cpu().numpy()
             if first is None:
                 first = o
             assert np.array_equal(o, first)
-        counters = ws.buf[: 4 * w.rows].view(torch.int32)
-        assert int(counters.abs().sum()) == 0, "arrival counters not reset"
     exp_out, _ = oracle_select(w)
     assert np.array_equal(first, exp_out)
 
@@ -338,7 +342,7 @@ def test_large_k_and_full_sort():
         x = np.round(rng.standard_normal((6, width)).astype(np.float32) * 4) / 4
         ke = rng.integers(0, width + 1, size=6).astype(np.int32)
         w = workloads.Workload(f"k{k}", x, None, ke, B, k, 1)
-        for plan in (1, 2):
+        for plan in (1, 2, 3):
             got, sc = gpu_select(w, plan, 7)
             exp_out, exp_sc = oracle_select(w)
             assert_same(got, sc, exp_out, exp_sc, f"k={k} plan {plan}")
@@ -353,3 +357,26 @@ def test_all_equal_scores_take_lowest_ids():
     assert got[1].tolist() == [1, 0] + [-1] * 8
     exp_out, _ = oracle_select(w)
     assert np.array_equal(got, exp_out)
+
+
+@pytest.mark.parametrize("plan", [1, 2, 3])
+def test_select_size_boundaries(plan):
+    """Rows whose candidate count sits on each side of the select's
+    register-slot boundaries (binary search up to 256 keys, radix above,
+    LDS-resident keys above 1024), with heavy ties and NaN/-inf."""
+    rng = np.random.default_rng(99)
+    B = 4
+    for n in (1, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 512, 513, 1023, 1024, 1025, 2000):
+        width = n * B
+        rows = 6
+        x = (rng.integers(0, 6, size=(rows, width)) / 2).astype(np.float32)
+        x[1, ::7] = np.nan
+        x[2] = -np.inf
+        x[3, : width // 2] = -np.inf
+        ke = np.full(rows, width, np.int32)
+        ke[4] = width - 3
+        for k in (1, 16, 64, min(n, 300)):
+            w = workloads.Workload(f"n{n}-k{k}", x, None, ke, B, k, 1)
+            got, sc = gpu_select(w, plan, 3)
+            exp_out, exp_sc = oracle_select(w)
+            assert_same(got, sc, exp_out, exp_sc, f"n={n} k={k} plan {plan}")
