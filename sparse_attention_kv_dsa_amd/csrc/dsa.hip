@@ -285,25 +285,185 @@ struct EmitScore {
 
 // ---------------------------------------------------------------- select --
 
-// Top-k over the score keys keys[0, nsel) of one row, by one wave.  KPL > 0
-// holds KPL rank keys per lane in registers (nsel <= 64*KPL); KPL == 0 reads
-// them from LDS on every pass.  Key i sits in lane i % 64, slot i / 64, so a
-// ballot over one slot lists ids in ascending order.  `scratch` is this
-// wave's LDS scratch: a 256-bin histogram, later the selected set
-// (max(256, 2*kcap) words, 16-byte aligned).
-template <int KPL>
-__device__ void select_wave(const uint32_t* keys, int32_t nsel, int32_t k, int32_t kcap,
-                            int32_t* out_row, uint32_t* scratch) {
-  const int lane = threadIdx.x & 63;
-  const int32_t nj = KPL > 0 ? KPL : (nsel + 63) >> 6;
-  uint32_t kv[KPL > 0 ? KPL : 1];
-  if constexpr (KPL > 0) {
+// Slot loops below are unrolled for the register-resident instantiations
+// (compile-time slot count); the LDS-resident one keeps a runtime count.
+#pragma clang diagnostic ignored "-Wpass-failed"
+
+// ---- one-wave select building blocks.  A "slot array" holds N keys per
+// lane; slot j of lane l is item j*64 + l, and items are in ascending block-id
+// order, so a ballot over one slot lists items in id order.
+
+// Rank of this lane's value among the 64 lane values, in descending order,
+// ties to the lower lane: a permutation of 0..63.  64 independent steps (no
+// loop-carried branch), each a broadcast of one lane's value.
+__device__ __forceinline__ uint32_t wave_rank_desc(uint32_t key) {
+  const uint32_t lane = threadIdx.x & 63;
+  uint32_t r = 0;
 #pragma unroll
-    for (int j = 0; j < KPL; ++j) {
-      const int32_t i = j * 64 + lane;
-      kv[j] = i < nsel ? rank_key(keys[i]) : 0u;
+  for (int j = 0; j < 64; ++j) {
+    const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)key, j);
+    r += (kj > key) | ((kj == key) & ((uint32_t)j < lane));
+  }
+  return r;
+}
+
+// Threshold of the keff largest among the slot array (keff < number of
+// nonzero keys): the selection is every key >= tg, then the first need_eq
+// keys equal to T in item order.  Bitwise binary search on the value with
+// wave ballots: T ends as the largest value with #(key >= T) >= keff; if a
+// probe has exactly keff keys at or above it, those keys are the selection.
+template <int N>
+__device__ __forceinline__ void threshold_search(const uint32_t* kv, uint32_t keff, uint32_t& tg,
+                                                 uint32_t& T, int32_t& need_eq) {
+  T = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int j = 0; j < N; ++j) cnt += (uint32_t)__popcll(__ballot(kv[j] >= cand));
+    if (cnt >= keff) {
+      T = cand;
+      if (cnt == keff) {
+        tg = T;
+        need_eq = 0;
+        return;
+      }
     }
   }
+  uint32_t above = 0;
+#pragma unroll
+  for (int j = 0; j < N; ++j) above += (uint32_t)__popcll(__ballot(kv[j] > T));
+  tg = T + 1u;
+  need_eq = (int32_t)(keff - above);
+}
+
+// Writes the selection to out_row[0, keff): keys >= tg (ordered by key
+// descending, then item order) followed by the first need_eq keys equal to
+// T.  id_at(j) gives slot j's block id.
+template <int N, class IdAt>
+__device__ __forceinline__ void emit_selection(const uint32_t* kv, const IdAt& id_at,
+                                               int32_t keff, uint32_t tg, uint32_t T,
+                                               int32_t need_eq, int32_t* out_row,
+                                               uint32_t* sel_key, uint32_t* sel_id) {
+  const int lane = threadIdx.x & 63;
+  const int32_t c_gt = keff - need_eq;
+  uint32_t pos_gt = 0, pos_eq = 0;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const uint32_t kj = kv[j];
+    const bool is_gt = kj >= tg && kj != 0u;
+    const bool is_eq = need_eq > 0 && kj == T && kj != 0u;
+    const uint64_t m_gt = __ballot(is_gt);
+    const uint64_t m_eq = __ballot(is_eq);
+    if (is_gt) {
+      const uint32_t r = pos_gt + lanes_below(m_gt);
+      sel_key[r] = kj;
+      sel_id[r] = id_at(j);
+    }
+    if (is_eq) {
+      const uint32_t r = pos_eq + lanes_below(m_eq);
+      if (r < (uint32_t)need_eq) out_row[c_gt + (int32_t)r] = (int32_t)id_at(j);
+    }
+    pos_gt += (uint32_t)__popcll(m_gt);
+    pos_eq += (uint32_t)__popcll(m_eq);
+  }
+  wave_sync();
+  // Order the outright selection: rank = #larger + #equal earlier in item
+  // order (sel_* is in item order).
+  if (c_gt <= 64) {
+    const uint32_t ki = lane < c_gt ? sel_key[lane] : 0u;
+    const uint32_t r = wave_rank_desc(ki);  // empty lanes hold 0 and rank last
+    if (lane < c_gt) out_row[r] = (int32_t)sel_id[lane];
+  } else {
+    for (int32_t i = lane; i < c_gt; i += 64) {
+      const uint32_t ki = sel_key[i];
+      int32_t r = 0;
+      for (int32_t j = 0; j < c_gt; ++j) {
+        const uint32_t kj = sel_key[j];
+        r += (kj > ki) || (kj == ki && j < i);
+      }
+      out_row[r] = (int32_t)sel_id[i];
+    }
+  }
+  wave_sync();
+}
+
+// Radix select (8-bit digits from the top) over the slot array given by
+// key_at(j), j < nj: `prefix` holds the digits fixed so far, `remaining` how
+// many keys are still needed among the keys that match it.  Same outputs as
+// threshold_search.  Used when the pruning below cannot shrink the set.
+template <int N, class KeyAt>
+__device__ __forceinline__ void threshold_radix(const KeyAt& key_at, int32_t nj_dyn, uint32_t keff,
+                                                uint32_t* hist, uint32_t& tg, uint32_t& T,
+                                                int32_t& need_eq) {
+  const int lane = threadIdx.x & 63;
+  const int32_t nj = N > 0 ? N : nj_dyn;  // compile-time for register slots
+  uint32_t prefix = 0u, remaining = keff;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+    wave_sync();
+    const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+#pragma unroll
+    for (int32_t j = 0; j < nj; ++j) {
+      const uint32_t kj = key_at(j);
+      if (kj != 0u && (kj & hmask) == prefix) atomicAdd(&hist[(kj >> shift) & 255u], 1u);
+    }
+    wave_sync();
+    // lane l holds bins 255-4l (q = 0) down to 252-4l (q = 3); `a0` counts the
+    // matching keys in higher bins (the lanes before this one)
+    const uint4 h = reinterpret_cast<const uint4*>(hist)[63 - lane];
+    const uint32_t tot = h.x + h.y + h.z + h.w;
+    uint32_t inc = tot;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t y = __shfl_up(inc, off);
+      if (lane >= off) inc += y;
+    }
+    const uint32_t a0 = inc - tot, a1 = a0 + h.w, a2 = a1 + h.z, a3 = a2 + h.y;
+    const bool h0 = a0 < remaining && remaining <= a1;
+    const bool h1 = a1 < remaining && remaining <= a2;
+    const bool h2 = a2 < remaining && remaining <= a3;
+    const bool h3 = a3 < remaining && remaining <= a3 + h.x;
+    const uint64_t hit = __ballot(h0 || h1 || h2 || h3);
+    const int src = (int)__builtin_ctzll(hit);  // exactly one lane holds the bucket
+    const uint32_t q = h0 ? 0u : (h1 ? 1u : (h2 ? 2u : 3u));
+    const uint32_t aq = h0 ? a0 : (h1 ? a1 : (h2 ? a2 : a3));
+    const uint32_t cq = h0 ? h.w : (h1 ? h.z : (h2 ? h.y : h.x));
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)(255u - 4u * lane - q), src);
+    const uint32_t rem = (uint32_t)__builtin_amdgcn_readlane((int)(remaining - aq), src);
+    const uint32_t cb = (uint32_t)__builtin_amdgcn_readlane((int)cq, src);
+    prefix |= d << shift;
+    wave_sync();
+    if (rem == cb) {  // the whole bucket is taken: every key >= prefix
+      tg = prefix;
+      T = 0u;
+      need_eq = 0;
+      return;
+    }
+    remaining = rem;
+  }
+  T = prefix;
+  tg = prefix + 1u;
+  need_eq = (int32_t)remaining;
+}
+
+// Top-k over the score keys keys[0, nsel) of one row, by one wave.  KPL > 0
+// holds KPL rank keys per lane in registers (nsel <= 64*KPL); KPL == 0 reads
+// them from LDS.  `scratch` is this wave's LDS scratch (select_scratch_words
+// words, 16-byte aligned): radix histogram, pruned candidates, selected set.
+template <int KPL>
+__device__ __forceinline__ void select_wave(const uint32_t* keys, int32_t nsel, int32_t k, int32_t kcap,
+                            int32_t* out_row, uint32_t* scratch) {
+  const int lane = threadIdx.x & 63;
+  constexpr int NR = KPL > 0 ? KPL : 1;
+  const int32_t nj = KPL > 0 ? KPL : (nsel + 63) >> 6;  // slots per lane
+  uint32_t kv[NR];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const int32_t i = j * 64 + lane;
+    kv[j] = (KPL > 0 && i < nsel) ? rank_key(keys[i]) : 0u;
+  }
+  auto slot_id = [lane](int32_t j) -> uint32_t { return (uint32_t)(j * 64 + lane); };
   auto key_at = [&](int32_t j) -> uint32_t {
     if constexpr (KPL > 0) {
       return kv[j];
@@ -312,146 +472,165 @@ __device__ void select_wave(const uint32_t* keys, int32_t nsel, int32_t k, int32
       return i < nsel ? rank_key(keys[i]) : 0u;
     }
   };
+  uint32_t* sel_key = scratch;
+  uint32_t* sel_id = scratch + kcap;
 
-  uint32_t nvalid = 0;
-  for (int32_t j = 0; j < nj; ++j) nvalid += (uint32_t)__popcll(__ballot(key_at(j) != 0u));
+  uint32_t nvalid = 0, lane_max = 0;
+#pragma unroll
+  for (int32_t j = 0; j < nj; ++j) {
+    const uint32_t kj = key_at(j);
+    nvalid += (uint32_t)__popcll(__ballot(kj != 0u));
+    lane_max = kj > lane_max ? kj : lane_max;
+  }
   const int32_t keff = (uint32_t)k < nvalid ? k : (int32_t)nvalid;
 
-  // The selection: every key >= tg, then the first need_eq keys equal to T
-  // in id order (need_eq > 0 only when ties at T straddle the k-th place).
-  uint32_t tg = 1u, T = 0u;
-  int32_t need_eq = 0;
-  if (keff > 0 && (uint32_t)keff < nvalid) {
-    if constexpr (KPL >= 1 && KPL <= 4) {
-      // Few keys: bitwise binary search on the threshold, registers only.
-      // T ends as the largest value with #(key >= T) >= keff; if some probe
-      // has exactly keff keys at or above it, those keys are the selection.
-      bool exact = false;
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = T | (1u << bit);
-        uint32_t cnt = 0;
-        for (int32_t j = 0; j < nj; ++j) cnt += (uint32_t)__popcll(__ballot(key_at(j) >= cand));
-        if (cnt >= (uint32_t)keff) {
-          T = cand;
-          if (cnt == (uint32_t)keff) {
-            exact = true;
-            break;
+  if (keff > 0) {
+    bool done = false;
+    if (keff <= 64) {
+      // At most 64 candidates, one per lane, then one all-pairs rank gives
+      // every output slot.  With more than 64 keys, the keff-th largest lane
+      // maximum is a lower bound on the keff-th largest key (keff lanes each
+      // hold a key at least that large), so only keys at or above it compete.
+      uint32_t ck = 0u, ci = 0u;
+      bool fits = false;
+      if constexpr (KPL == 1) {
+        ck = kv[0];
+        ci = (uint32_t)lane;
+        fits = true;
+      } else {
+        const uint64_t at = __ballot(wave_rank_desc(lane_max) == (uint32_t)(keff - 1));
+        const uint32_t t0 = (uint32_t)__builtin_amdgcn_readlane((int)lane_max, (int)__builtin_ctzll(at));
+        const uint32_t lb = t0 > 1u ? t0 : 1u;
+        uint32_t ncand = 0;
+#pragma unroll
+        for (int32_t j = 0; j < nj; ++j) ncand += (uint32_t)__popcll(__ballot(key_at(j) >= lb));
+        if (ncand <= 64) {
+          uint32_t* cand_key = scratch;
+          uint32_t* cand_id = scratch + 64;
+          uint32_t pos = 0;
+#pragma unroll
+          for (int32_t j = 0; j < nj; ++j) {
+            const uint32_t kj = key_at(j);
+            const bool c = kj >= lb;
+            const uint64_t m = __ballot(c);
+            if (c) {
+              const uint32_t r = pos + lanes_below(m);
+              cand_key[r] = kj;
+              cand_id[r] = (uint32_t)(j * 64 + lane);
+            }
+            pos += (uint32_t)__popcll(m);
           }
+          wave_sync();
+          ck = (uint32_t)lane < ncand ? cand_key[lane] : 0u;
+          ci = (uint32_t)lane < ncand ? cand_id[lane] : 0u;
+          wave_sync();
+          fits = true;
         }
       }
-      if (exact) {
-        tg = T;
-      } else {
-        uint32_t above = 0;
-        for (int32_t j = 0; j < nj; ++j) above += (uint32_t)__popcll(__ballot(key_at(j) > T));
-        tg = T + 1u;
-        need_eq = keff - (int32_t)above;
+      if (fits) {
+        const uint32_t r = wave_rank_desc(ck);  // empty lanes hold 0 and rank last
+        if (ck != 0u && r < (uint32_t)keff) out_row[r] = (int32_t)ci;
+        done = true;
       }
-    } else {
-      // Radix select, 8-bit digits from the top: `prefix` holds the digits
-      // fixed so far, `remaining` how many keys are still needed among the
-      // keys that match it (all keys above it are already in).  Ends with
-      // either a whole bucket taken (the selection is every key >= tg) or the
-      // exact keff-th largest key T (keys > T, then the first need_eq keys
-      // equal to T).
-      uint32_t* hist = scratch;
-      uint32_t prefix = 0u, remaining = (uint32_t)keff;
-      bool whole = false;
-      for (int shift = 24; shift >= 0; shift -= 8) {
-        reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
-        wave_sync();
-        const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    }
+    if (!done && (uint32_t)keff == nvalid) {
+      // every candidate block is selected (LDS-resident keys: below)
+      if constexpr (KPL > 0) {
+        emit_selection<KPL>(kv, slot_id, keff, 1u, 0u, 0, out_row, sel_key, sel_id);
+        done = true;
+      }
+    } else if (!done && KPL >= 1 && KPL <= 4) {
+      uint32_t tg, T;
+      int32_t need_eq;
+      threshold_search<NR>(kv, (uint32_t)keff, tg, T, need_eq);
+      emit_selection<NR>(kv, slot_id, keff, tg, T, need_eq, out_row, sel_key, sel_id);
+      done = true;
+    } else if (!done && keff <= 64) {
+      // More than 64 candidates after pruning (heavy ties): up to 256 of
+      // them, four per lane, with the binary-search threshold.
+      const uint32_t lm[1] = {lane_max};
+      uint32_t unused_tg, t0;
+      int32_t unused_eq;
+      threshold_search<1>(lm, (uint32_t)keff, unused_tg, t0, unused_eq);
+      const uint32_t lb = t0 > 1u ? t0 : 1u;
+      uint32_t ncand = 0;
+#pragma unroll
+      for (int32_t j = 0; j < nj; ++j) ncand += (uint32_t)__popcll(__ballot(key_at(j) >= lb));
+      if (ncand <= 256) {
+        // compact the candidates in id order, then select among them
+        uint32_t* cand_key = scratch;
+        uint32_t* cand_id = scratch + 256;
+        uint32_t pos = 0;
+#pragma unroll
         for (int32_t j = 0; j < nj; ++j) {
           const uint32_t kj = key_at(j);
-          if (kj != 0u && (kj & hmask) == prefix) atomicAdd(&hist[(kj >> shift) & 255u], 1u);
+          const bool c = kj >= lb;
+          const uint64_t m = __ballot(c);
+          if (c) {
+            const uint32_t r = pos + lanes_below(m);
+            cand_key[r] = kj;
+            cand_id[r] = (uint32_t)(j * 64 + lane);
+          }
+          pos += (uint32_t)__popcll(m);
         }
         wave_sync();
-        // lane l holds bins 255-4l (q = 0) down to 252-4l (q = 3); `above` is
-        // the number of matching keys in higher bins (lanes before this one)
-        const uint4 h = reinterpret_cast<const uint4*>(hist)[63 - lane];
-        const uint32_t tot = h.x + h.y + h.z + h.w;
-        uint32_t inc = tot;
+        uint32_t ck[4], ci[4];
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t y = __shfl_up(inc, off);
-          if (lane >= off) inc += y;
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t i = (uint32_t)(j * 64 + lane);
+          ck[j] = i < ncand ? cand_key[i] : 0u;
+          ci[j] = i < ncand ? cand_id[i] : 0u;
         }
-        const uint32_t a0 = inc - tot, a1 = a0 + h.w, a2 = a1 + h.z, a3 = a2 + h.y;
-        const bool h0 = a0 < remaining && remaining <= a1;
-        const bool h1 = a1 < remaining && remaining <= a2;
-        const bool h2 = a2 < remaining && remaining <= a3;
-        const bool h3 = a3 < remaining && remaining <= a3 + h.x;
-        const uint64_t hit = __ballot(h0 || h1 || h2 || h3);
-        const int src = (int)__builtin_ctzll(hit);  // exactly one lane holds the bucket
-        const uint32_t q = h0 ? 0u : (h1 ? 1u : (h2 ? 2u : 3u));
-        const uint32_t aq = h0 ? a0 : (h1 ? a1 : (h2 ? a2 : a3));
-        const uint32_t cq = h0 ? h.w : (h1 ? h.z : (h2 ? h.y : h.x));
-        const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)(255u - 4u * lane - q), src);
-        const uint32_t rem = (uint32_t)__builtin_amdgcn_readlane((int)(remaining - aq), src);
-        const uint32_t cb = (uint32_t)__builtin_amdgcn_readlane((int)cq, src);
-        prefix |= d << shift;
-        wave_sync();
-        if (rem == cb) {
-          whole = true;
-          break;
-        }
-        remaining = rem;
+        wave_sync();  // the candidate area is reused for the selected set
+        uint32_t tg = 1u, T = 0u;
+        int32_t need_eq = 0;
+        if ((uint32_t)keff < ncand) threshold_search<4>(ck, (uint32_t)keff, tg, T, need_eq);
+        emit_selection<4>(ck, [&ci](int32_t j) { return ci[j]; }, keff, tg, T, need_eq, out_row,
+                         sel_key, sel_id);
+        done = true;
       }
-      if (whole) {
-        tg = prefix;
+    }
+    if (!done) {
+      uint32_t tg = 1u, T = 0u;
+      int32_t need_eq = 0;
+      if ((uint32_t)keff < nvalid)
+        threshold_radix<KPL>(key_at, nj, (uint32_t)keff, scratch, tg, T, need_eq);
+      if constexpr (KPL > 0) {
+        emit_selection<KPL>(kv, slot_id, keff, tg, T, need_eq, out_row, sel_key, sel_id);
       } else {
-        T = prefix;
-        tg = prefix + 1u;
-        need_eq = (int32_t)remaining;
-      }
-    }
-  }
-  const int32_t c_gt = keff - need_eq;
-
-  // Compaction in id order: keys >= tg into sel_*, the first need_eq keys
-  // equal to T straight to their final slots after them.
-  if (keff > 0) {
-    uint32_t* sel_key = scratch;
-    uint32_t* sel_id = scratch + kcap;
-    uint32_t pos_gt = 0, pos_eq = 0;
-    for (int32_t j = 0; j < nj; ++j) {
-      const uint32_t kj = key_at(j);
-      const bool is_gt = kj >= tg && kj != 0u;
-      const bool is_eq = need_eq > 0 && kj == T;
-      const uint64_t m_gt = __ballot(is_gt);
-      const uint64_t m_eq = __ballot(is_eq);
-      if (is_gt) {
-        const uint32_t r = pos_gt + lanes_below(m_gt);
-        sel_key[r] = kj;
-        sel_id[r] = (uint32_t)(j * 64 + lane);
-      }
-      if (is_eq) {
-        const uint32_t r = pos_eq + lanes_below(m_eq);
-        if (r < (uint32_t)need_eq) out_row[c_gt + (int32_t)r] = j * 64 + lane;
-      }
-      pos_gt += (uint32_t)__popcll(m_gt);
-      pos_eq += (uint32_t)__popcll(m_eq);
-    }
-    wave_sync();
-    // Order the outright selection: rank = #larger + #equal with a smaller id
-    // (sel_* is in id order).
-    if (c_gt <= 64) {
-      const uint32_t ki = lane < c_gt ? sel_key[lane] : 0u;
-      int32_t r = 0;
-      for (int32_t j = 0; j < c_gt; ++j) {
-        const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)ki, j);
-        r += (kj > ki) || (kj == ki && j < lane);
-      }
-      if (lane < c_gt) out_row[r] = (int32_t)sel_id[lane];
-    } else {
-      for (int32_t i = lane; i < c_gt; i += 64) {
-        const uint32_t ki = sel_key[i];
-        int32_t r = 0;
-        for (int32_t j = 0; j < c_gt; ++j) {
-          const uint32_t kj = sel_key[j];
-          r += (kj > ki) || (kj == ki && j < i);
+        // LDS-resident keys: the same emission, one slot at a time
+        const int32_t c_gt = keff - need_eq;
+        uint32_t pos_gt = 0, pos_eq = 0;
+#pragma unroll
+        for (int32_t j = 0; j < nj; ++j) {
+          const uint32_t kj = key_at(j);
+          const bool is_gt = kj >= tg && kj != 0u;
+          const bool is_eq = need_eq > 0 && kj == T && kj != 0u;
+          const uint64_t m_gt = __ballot(is_gt);
+          const uint64_t m_eq = __ballot(is_eq);
+          if (is_gt) {
+            const uint32_t r = pos_gt + lanes_below(m_gt);
+            sel_key[r] = kj;
+            sel_id[r] = (uint32_t)(j * 64 + lane);
+          }
+          if (is_eq) {
+            const uint32_t r = pos_eq + lanes_below(m_eq);
+            if (r < (uint32_t)need_eq) out_row[c_gt + (int32_t)r] = j * 64 + lane;
+          }
+          pos_gt += (uint32_t)__popcll(m_gt);
+          pos_eq += (uint32_t)__popcll(m_eq);
         }
-        out_row[r] = (int32_t)sel_id[i];
+        wave_sync();
+        for (int32_t i = lane; i < c_gt; i += 64) {
+          const uint32_t ki = sel_key[i];
+          int32_t r = 0;
+          for (int32_t j = 0; j < c_gt; ++j) {
+            const uint32_t kj = sel_key[j];
+            r += (kj > ki) || (kj == ki && j < i);
+          }
+          out_row[r] = (int32_t)sel_id[i];
+        }
+        wave_sync();
       }
     }
   }
@@ -461,7 +640,8 @@ __device__ void select_wave(const uint32_t* keys, int32_t nsel, int32_t k, int32
 // One wave finishes a row whose keys[0, nvb) hold the streamed block keys:
 // -inf up to nsel, pin, optional score write-back, select.  `wmem` is this
 // row's LDS state: keys (keys_words), then the select scratch.
-__device__ void finish_row_wave(const Params& p, int64_t r, const RowGeom& g, uint32_t* wmem) {
+__device__ __forceinline__ void finish_row_wave(const Params& p, int64_t r, const RowGeom& g,
+                                                uint32_t* wmem) {
   const int lane = threadIdx.x & 63;
   uint32_t* keys = wmem;
   for (int32_t b = g.nvb + lane; b < g.nsel; b += 64) keys[b] = kKeyNegInf;
@@ -669,13 +849,13 @@ int64_t select_kcap(int64_t nblocks, int32_t k) {
 }
 
 // LDS words of one row's select state: keys, then a scratch that holds the
-// radix histogram (256 words) and later the selected keys and ids; a
-// multiple of 4 words.
+// radix histogram (256 words) or the pruned candidates (2 x 256 words), and
+// later the selected keys and ids (2 x kcap); a multiple of 4 words.
 int64_t select_keys_words(int64_t nblocks) { return cdiv(nblocks, 4) * 4; }
 
 int64_t select_wave_words(int64_t nblocks, int32_t k) {
   const int64_t sel = 2 * select_kcap(nblocks, k);
-  return select_keys_words(nblocks) + cdiv(sel > 256 ? sel : 256, 4) * 4;
+  return select_keys_words(nblocks) + cdiv(sel > 512 ? sel : 512, 4) * 4;
 }
 
 // Plan ids (also the values of dsa_select_candidate_blocks_plan's `plan`).
