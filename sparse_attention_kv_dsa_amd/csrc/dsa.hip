@@ -17,20 +17,21 @@
 //     16-lane row, ds_swizzle across rows and a bpermute across halves.
 //   * Scores are kept as order-preserving uint32 keys (unsigned order ==
 //     float order, canonical NaN on top), in LDS for the select.
-//   * Top-k runs in one wave with no barrier: the row's rank keys sit in
-//     registers, an 8-bit-digit radix select (LDS histogram per pass, lane
-//     prefix scan, early exit when a whole bucket is taken) finds the k-th
-//     largest, candidates are compacted in block-id order with ballot/mbcnt
-//     (so ties resolve to the lowest ids), and the ones above the threshold
-//     are ordered by counting rank.
+//   * Top-k prunes, then ranks: the k-th largest of at most 64*gpl group
+//     maxima bounds the k-th largest key from below, the keys at or above it
+//     (the candidates) are compacted into LDS as distinct 64-bit words
+//     (key, inverted block id), and a candidate's output slot is the number
+//     of larger words.  Every wave of a row's workgroup takes part; rows with
+//     more candidates than the LDS holds fall back to an exact one-wave radix
+//     select.
 //   * Launch plans: short rows take one wave per row (four rows per
-//     workgroup, no barrier at all); long rows take a workgroup whose four
-//     waves stream the row and hand the keys to one selecting wave; few long
-//     rows (decode) are split in chunks over many CUs by a streaming kernel
-//     that writes the block keys, and a second kernel selects.  Cross-CU
-//     hand-off inside one kernel would need agent-scope fences, which on
-//     this chip write back and invalidate a whole XCD's L2 each; the kernel
-//     boundary is the cheaper synchronisation.
+//     workgroup, no barrier at all); long rows take a workgroup whose waves
+//     stream the row into LDS and then select it together; few long rows
+//     (decode) are split in chunks over many CUs by a streaming kernel that
+//     writes the block keys, and a second kernel selects, one workgroup per
+//     row.  Cross-CU hand-off inside one kernel would need agent-scope
+//     fences, which on this chip write back and invalidate a whole XCD's L2
+//     each; the kernel boundary is the cheaper synchronisation.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -113,7 +114,7 @@ struct Params {
   int32_t vec_ok;      // width % 4 == 0: float4 loads never cross the row's end
   int32_t kcap;        // max(1, min(k, nblocks)): selected-set capacity
   int32_t keys_words;  // LDS words for one row's keys (nblocks rounded up to 4)
-  int32_t wave_words;  // LDS words of one row's select state (keys + scratch)
+  int32_t wave_words;  // LDS words of one row's select state (keys, control, area)
   int32_t* out;
   int64_t ld_out;
   float* scores;  // block-scores output, or the optional write-back
@@ -284,128 +285,141 @@ struct EmitScore {
 };
 
 // ---------------------------------------------------------------- select --
+//
+// Top-k of one row's block keys, in four steps with no sort of the whole row:
+//  (A) every key becomes a rank key (-inf -> 0 "no candidate", -0 -> +0);
+//      aligned groups of lanes take their maximum, giving at most 64*gpl
+//      group maxima;
+//  (C) T0 = the keff-th largest group maximum, keff = min(k, #nonzero keys).
+//      keff groups each hold a key >= T0, so T0 is a lower bound on the
+//      keff-th largest key: every selected key is >= T0;
+//  (E) the keys >= T0 (the candidates, few for any spread of values) are
+//      compacted into LDS as 64-bit words (rank key << 32 | ~block id), which
+//      are distinct and order exactly as the selection order (key descending,
+//      then id ascending);
+//  (G) each candidate's rank is the count of larger words; ranks < keff give
+//      the output slots directly.
+// More than kCandCap candidates (heavy ties at T0, or k in the hundreds)
+// fall back to an exact one-wave radix select over the LDS keys.
 
-// Slot loops below are unrolled for the register-resident instantiations
-// (compile-time slot count); the LDS-resident one keeps a runtime count.
-#pragma clang diagnostic ignored "-Wpass-failed"
+constexpr int kCtlWords = 32;   // per-row control words in LDS
+constexpr int kCtlValid = 0;    // #nonzero rank keys (atomic)
+constexpr int kCtlCand = 1;     // #candidates (atomic)
+constexpr int kCtlT0 = 2;       // candidate threshold
+constexpr int kCtlKeff = 3;     // min(k, #nonzero)
+constexpr int kCandCap = 256;   // candidates held in LDS
+constexpr int kAreaMinWords = 2 * kCandCap;
 
-// ---- one-wave select building blocks.  A "slot array" holds N keys per
-// lane; slot j of lane l is item j*64 + l, and items are in ascending block-id
-// order, so a ballot over one slot lists items in id order.
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
-// Rank of this lane's value among the 64 lane values, in descending order,
-// ties to the lower lane: a permutation of 0..63.  64 independent steps (no
-// loop-carried branch), each a broadcast of one lane's value.
-__device__ __forceinline__ uint32_t wave_rank_desc(uint32_t key) {
-  const uint32_t lane = threadIdx.x & 63;
-  uint32_t r = 0;
-#pragma unroll
-  for (int j = 0; j < 64; ++j) {
-    const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)key, j);
-    r += (kj > key) | ((kj == key) & ((uint32_t)j < lane));
-  }
-  return r;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 
-// Threshold of the keff largest among the slot array (keff < number of
-// nonzero keys): the selection is every key >= tg, then the first need_eq
-// keys equal to T in item order.  Bitwise binary search on the value with
-// wave ballots: T ends as the largest value with #(key >= T) >= keff; if a
-// probe has exactly keff keys at or above it, those keys are the selection.
+// Maximum over aligned groups of G lanes (G a power of two <= 64); every lane
+// of a group ends with the group's value.  All 64 lanes must be active.
+template <int G>
+__device__ __forceinline__ uint32_t group_umax(uint32_t v) {
+  if constexpr (G >= 2) v = umax(v, dpp_u32<0xB1>(v));    // quad_perm [1,0,3,2]
+  if constexpr (G >= 4) v = umax(v, dpp_u32<0x4E>(v));    // quad_perm [2,3,0,1]
+  if constexpr (G >= 8) v = umax(v, dpp_u32<0x141>(v));   // row_half_mirror
+  if constexpr (G >= 16) v = umax(v, dpp_u32<0x140>(v));  // row_mirror
+  if constexpr (G >= 32) v = umax(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));
+  if constexpr (G >= 64) v = umax(v, (uint32_t)__shfl_xor((int)v, 32));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t group_umax_dyn(uint32_t v, int gl) {
+  switch (gl) {
+    case 1: return v;
+    case 2: return group_umax<2>(v);
+    case 4: return group_umax<4>(v);
+    case 8: return group_umax<8>(v);
+    case 16: return group_umax<16>(v);
+    case 32: return group_umax<32>(v);
+    default: return group_umax<64>(v);
+  }
+}
+
+template <bool WG>
+__device__ __forceinline__ void row_barrier() {
+  if constexpr (WG) __syncthreads();
+  else wave_sync();
+}
+
+// Score key of block i < nsel of a row whose blocks [0, nvb) sit in keys[].
+__device__ __forceinline__ uint32_t block_key(const uint32_t* keys, const RowGeom& g, int32_t i) {
+  return i == g.pin ? kKeyPosInf : (i < g.nvb ? keys[i] : kKeyNegInf);
+}
+
+// Candidate word: rank key above, inverted id below; 0 for a non-candidate.
+__device__ __forceinline__ uint64_t cand_word(uint32_t rk, uint32_t i) {
+  return rk ? (((uint64_t)rk << 32) | (uint64_t)(~i)) : 0ull;
+}
+
+// Bitwise binary search with ballots over N values per lane: the largest T
+// with #(value >= T) >= need (0 if no T >= 1 qualifies).  Once a probe has
+// exactly `need` values at or above it, T is the smallest of those values.
 template <int N>
-__device__ __forceinline__ void threshold_search(const uint32_t* kv, uint32_t keff, uint32_t& tg,
-                                                 uint32_t& T, int32_t& need_eq) {
-  T = 0u;
+__device__ __forceinline__ uint32_t kth_largest_search(const uint32_t* kv, uint32_t need) {
+  uint32_t T = 0u;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = T | (1u << bit);
     uint32_t cnt = 0;
 #pragma unroll
     for (int j = 0; j < N; ++j) cnt += (uint32_t)__popcll(__ballot(kv[j] >= cand));
-    if (cnt >= keff) {
+    if (cnt >= need) {
       T = cand;
-      if (cnt == keff) {
-        tg = T;
-        need_eq = 0;
-        return;
+      if (cnt == need) {
+        uint32_t inv = 0u;  // max of ~v over v >= cand, i.e. ~min
+#pragma unroll
+        for (int j = 0; j < N; ++j) inv = umax(inv, kv[j] >= cand ? ~kv[j] : 0u);
+        return ~(uint32_t)__builtin_amdgcn_readfirstlane((int)group_umax<64>(inv));
       }
     }
   }
-  uint32_t above = 0;
-#pragma unroll
-  for (int j = 0; j < N; ++j) above += (uint32_t)__popcll(__ballot(kv[j] > T));
-  tg = T + 1u;
-  need_eq = (int32_t)(keff - above);
+  return T;
 }
 
-// Writes the selection to out_row[0, keff): keys >= tg (ordered by key
-// descending, then item order) followed by the first need_eq keys equal to
-// T.  id_at(j) gives slot j's block id.
-template <int N, class IdAt>
-__device__ __forceinline__ void emit_selection(const uint32_t* kv, const IdAt& id_at,
-                                               int32_t keff, uint32_t tg, uint32_t T,
-                                               int32_t need_eq, int32_t* out_row,
-                                               uint32_t* sel_key, uint32_t* sel_id) {
+// Ranks cand[0, ncand) (distinct words, 0 = empty): slot r < keff of the
+// output takes the id of the word with r larger words.  Wave `wave` of `nw`
+// takes every nw-th group of 64 candidates.
+__device__ __forceinline__ void rank_candidates(const uint64_t* cand, int32_t ncand, int32_t keff,
+                                                int32_t* out_row, int wave, int nw) {
   const int lane = threadIdx.x & 63;
-  const int32_t c_gt = keff - need_eq;
-  uint32_t pos_gt = 0, pos_eq = 0;
-#pragma unroll
-  for (int j = 0; j < N; ++j) {
-    const uint32_t kj = kv[j];
-    const bool is_gt = kj >= tg && kj != 0u;
-    const bool is_eq = need_eq > 0 && kj == T && kj != 0u;
-    const uint64_t m_gt = __ballot(is_gt);
-    const uint64_t m_eq = __ballot(is_eq);
-    if (is_gt) {
-      const uint32_t r = pos_gt + lanes_below(m_gt);
-      sel_key[r] = kj;
-      sel_id[r] = id_at(j);
+  const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(cand);
+  for (int32_t base = wave * 64; base < ncand; base += nw * 64) {
+    const int32_t idx = base + lane;
+    const uint64_t ci = idx < ncand ? cand[idx] : 0ull;
+    uint32_t r = 0;
+    int32_t j = 0;
+    for (; j + 8 <= ncand; j += 8) {  // broadcast reads, four in flight
+      const ulonglong2 a = c2[(j >> 1) + 0], b = c2[(j >> 1) + 1];
+      const ulonglong2 c = c2[(j >> 1) + 2], d = c2[(j >> 1) + 3];
+      r += (uint32_t)(a.x > ci) + (uint32_t)(a.y > ci) + (uint32_t)(b.x > ci) + (uint32_t)(b.y > ci) +
+           (uint32_t)(c.x > ci) + (uint32_t)(c.y > ci) + (uint32_t)(d.x > ci) + (uint32_t)(d.y > ci);
     }
-    if (is_eq) {
-      const uint32_t r = pos_eq + lanes_below(m_eq);
-      if (r < (uint32_t)need_eq) out_row[c_gt + (int32_t)r] = (int32_t)id_at(j);
-    }
-    pos_gt += (uint32_t)__popcll(m_gt);
-    pos_eq += (uint32_t)__popcll(m_eq);
+    for (; j < ncand; ++j) r += (uint32_t)(cand[j] > ci);
+    if (idx < ncand && ci != 0ull && r < (uint32_t)keff) out_row[r] = (int32_t)(~(uint32_t)ci);
   }
-  wave_sync();
-  // Order the outright selection: rank = #larger + #equal earlier in item
-  // order (sel_* is in item order).
-  if (c_gt <= 64) {
-    const uint32_t ki = lane < c_gt ? sel_key[lane] : 0u;
-    const uint32_t r = wave_rank_desc(ki);  // empty lanes hold 0 and rank last
-    if (lane < c_gt) out_row[r] = (int32_t)sel_id[lane];
-  } else {
-    for (int32_t i = lane; i < c_gt; i += 64) {
-      const uint32_t ki = sel_key[i];
-      int32_t r = 0;
-      for (int32_t j = 0; j < c_gt; ++j) {
-        const uint32_t kj = sel_key[j];
-        r += (kj > ki) || (kj == ki && j < i);
-      }
-      out_row[r] = (int32_t)sel_id[i];
-    }
-  }
-  wave_sync();
 }
 
-// Radix select (8-bit digits from the top) over the slot array given by
-// key_at(j), j < nj: `prefix` holds the digits fixed so far, `remaining` how
-// many keys are still needed among the keys that match it.  Same outputs as
-// threshold_search.  Used when the pruning below cannot shrink the set.
-template <int N, class KeyAt>
-__device__ __forceinline__ void threshold_radix(const KeyAt& key_at, int32_t nj_dyn, uint32_t keff,
-                                                uint32_t* hist, uint32_t& tg, uint32_t& T,
-                                                int32_t& need_eq) {
+// Radix select (8-bit digits from the top) over the LDS rank keys of one
+// wave's slot array (slot j of lane l is key j*64 + l): the selection is every
+// key >= tg, then the first need_eq keys equal to T in id order.
+__device__ void threshold_radix_lds(const uint32_t* keys, int32_t nsel, uint32_t keff,
+                                    uint32_t* hist, uint32_t& tg, uint32_t& T, int32_t& need_eq) {
   const int lane = threadIdx.x & 63;
-  const int32_t nj = N > 0 ? N : nj_dyn;  // compile-time for register slots
+  const int32_t nj = (nsel + 63) >> 6;
   uint32_t prefix = 0u, remaining = keff;
   for (int shift = 24; shift >= 0; shift -= 8) {
     reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
     wave_sync();
     const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
-#pragma unroll
     for (int32_t j = 0; j < nj; ++j) {
-      const uint32_t kj = key_at(j);
+      const int32_t i = j * 64 + lane;
+      const uint32_t kj = i < nsel ? rank_key(keys[i]) : 0u;
       if (kj != 0u && (kj & hmask) == prefix) atomicAdd(&hist[(kj >> shift) & 255u], 1u);
     }
     wave_sync();
@@ -447,252 +461,225 @@ __device__ __forceinline__ void threshold_radix(const KeyAt& key_at, int32_t nj_
   need_eq = (int32_t)remaining;
 }
 
-// Top-k over the score keys keys[0, nsel) of one row, by one wave.  KPL > 0
-// holds KPL rank keys per lane in registers (nsel <= 64*KPL); KPL == 0 reads
-// them from LDS.  `scratch` is this wave's LDS scratch (select_scratch_words
-// words, 16-byte aligned): radix histogram, pruned candidates, selected set.
-template <int KPL>
-__device__ __forceinline__ void select_wave(const uint32_t* keys, int32_t nsel, int32_t k, int32_t kcap,
-                            int32_t* out_row, uint32_t* scratch) {
+// Exact top-k by one wave over LDS keys[0, nsel) (pin and -inf fill already
+// in place), for rows the candidate bound cannot shrink to kCandCap.
+// `scratch`: 16-byte aligned, max(512, 2*kcap) words.
+__device__ void select_wave_exact(const uint32_t* keys, int32_t nsel, int32_t k, int32_t kcap,
+                                  int32_t* out_row, uint32_t* scratch) {
   const int lane = threadIdx.x & 63;
-  constexpr int NR = KPL > 0 ? KPL : 1;
-  const int32_t nj = KPL > 0 ? KPL : (nsel + 63) >> 6;  // slots per lane
-  uint32_t kv[NR];
-#pragma unroll
-  for (int j = 0; j < NR; ++j) {
-    const int32_t i = j * 64 + lane;
-    kv[j] = (KPL > 0 && i < nsel) ? rank_key(keys[i]) : 0u;
-  }
-  auto slot_id = [lane](int32_t j) -> uint32_t { return (uint32_t)(j * 64 + lane); };
-  auto key_at = [&](int32_t j) -> uint32_t {
-    if constexpr (KPL > 0) {
-      return kv[j];
-    } else {
-      const int32_t i = j * 64 + lane;
-      return i < nsel ? rank_key(keys[i]) : 0u;
-    }
-  };
-  uint32_t* sel_key = scratch;
-  uint32_t* sel_id = scratch + kcap;
-
-  uint32_t nvalid = 0, lane_max = 0;
-#pragma unroll
+  const int32_t nj = (nsel + 63) >> 6;
+  uint32_t nvalid = 0;
   for (int32_t j = 0; j < nj; ++j) {
-    const uint32_t kj = key_at(j);
-    nvalid += (uint32_t)__popcll(__ballot(kj != 0u));
-    lane_max = kj > lane_max ? kj : lane_max;
+    const int32_t i = j * 64 + lane;
+    nvalid += (uint32_t)__popcll(__ballot(i < nsel && rank_key(keys[i]) != 0u));
   }
   const int32_t keff = (uint32_t)k < nvalid ? k : (int32_t)nvalid;
-
   if (keff > 0) {
-    bool done = false;
-    if (keff <= 64) {
-      // At most 64 candidates, one per lane, then one all-pairs rank gives
-      // every output slot.  With more than 64 keys, the keff-th largest lane
-      // maximum is a lower bound on the keff-th largest key (keff lanes each
-      // hold a key at least that large), so only keys at or above it compete.
-      uint32_t ck = 0u, ci = 0u;
-      bool fits = false;
-      if constexpr (KPL == 1) {
-        ck = kv[0];
-        ci = (uint32_t)lane;
-        fits = true;
-      } else {
-        const uint64_t at = __ballot(wave_rank_desc(lane_max) == (uint32_t)(keff - 1));
-        const uint32_t t0 = (uint32_t)__builtin_amdgcn_readlane((int)lane_max, (int)__builtin_ctzll(at));
-        const uint32_t lb = t0 > 1u ? t0 : 1u;
-        uint32_t ncand = 0;
-#pragma unroll
-        for (int32_t j = 0; j < nj; ++j) ncand += (uint32_t)__popcll(__ballot(key_at(j) >= lb));
-        if (ncand <= 64) {
-          uint32_t* cand_key = scratch;
-          uint32_t* cand_id = scratch + 64;
-          uint32_t pos = 0;
-#pragma unroll
-          for (int32_t j = 0; j < nj; ++j) {
-            const uint32_t kj = key_at(j);
-            const bool c = kj >= lb;
-            const uint64_t m = __ballot(c);
-            if (c) {
-              const uint32_t r = pos + lanes_below(m);
-              cand_key[r] = kj;
-              cand_id[r] = (uint32_t)(j * 64 + lane);
-            }
-            pos += (uint32_t)__popcll(m);
-          }
-          wave_sync();
-          ck = (uint32_t)lane < ncand ? cand_key[lane] : 0u;
-          ci = (uint32_t)lane < ncand ? cand_id[lane] : 0u;
-          wave_sync();
-          fits = true;
-        }
+    uint32_t tg = 1u, T = 0u;
+    int32_t need_eq = 0;
+    if ((uint32_t)keff < nvalid) threshold_radix_lds(keys, nsel, (uint32_t)keff, scratch, tg, T, need_eq);
+    // keys >= tg go to sel_* in id order; the first need_eq keys equal to T
+    // fill the last slots directly
+    uint32_t* sel_key = scratch;
+    uint32_t* sel_id = scratch + kcap;
+    const int32_t c_gt = keff - need_eq;
+    uint32_t pos_gt = 0, pos_eq = 0;
+    for (int32_t j = 0; j < nj; ++j) {
+      const int32_t i = j * 64 + lane;
+      const uint32_t kj = i < nsel ? rank_key(keys[i]) : 0u;
+      const bool is_gt = kj >= tg && kj != 0u;
+      const bool is_eq = need_eq > 0 && kj == T && kj != 0u;
+      const uint64_t m_gt = __ballot(is_gt);
+      const uint64_t m_eq = __ballot(is_eq);
+      if (is_gt) {
+        const uint32_t r = pos_gt + lanes_below(m_gt);
+        sel_key[r] = kj;
+        sel_id[r] = (uint32_t)i;
       }
-      if (fits) {
-        const uint32_t r = wave_rank_desc(ck);  // empty lanes hold 0 and rank last
-        if (ck != 0u && r < (uint32_t)keff) out_row[r] = (int32_t)ci;
-        done = true;
+      if (is_eq) {
+        const uint32_t r = pos_eq + lanes_below(m_eq);
+        if (r < (uint32_t)need_eq) out_row[c_gt + (int32_t)r] = i;
       }
+      pos_gt += (uint32_t)__popcll(m_gt);
+      pos_eq += (uint32_t)__popcll(m_eq);
     }
-    if (!done && (uint32_t)keff == nvalid) {
-      // every candidate block is selected (LDS-resident keys: below)
-      if constexpr (KPL > 0) {
-        emit_selection<KPL>(kv, slot_id, keff, 1u, 0u, 0, out_row, sel_key, sel_id);
-        done = true;
+    wave_sync();
+    // order the outright selection: rank = #larger + #equal earlier in id order
+    for (int32_t i = lane; i < c_gt; i += 64) {
+      const uint32_t ki = sel_key[i];
+      int32_t r = 0;
+      for (int32_t j = 0; j < c_gt; ++j) {
+        const uint32_t kj = sel_key[j];
+        r += (kj > ki) || (kj == ki && j < i);
       }
-    } else if (!done && KPL >= 1 && KPL <= 4) {
-      uint32_t tg, T;
-      int32_t need_eq;
-      threshold_search<NR>(kv, (uint32_t)keff, tg, T, need_eq);
-      emit_selection<NR>(kv, slot_id, keff, tg, T, need_eq, out_row, sel_key, sel_id);
-      done = true;
-    } else if (!done && keff <= 64) {
-      // More than 64 candidates after pruning (heavy ties): up to 256 of
-      // them, four per lane, with the binary-search threshold.
-      const uint32_t lm[1] = {lane_max};
-      uint32_t unused_tg, t0;
-      int32_t unused_eq;
-      threshold_search<1>(lm, (uint32_t)keff, unused_tg, t0, unused_eq);
-      const uint32_t lb = t0 > 1u ? t0 : 1u;
-      uint32_t ncand = 0;
-#pragma unroll
-      for (int32_t j = 0; j < nj; ++j) ncand += (uint32_t)__popcll(__ballot(key_at(j) >= lb));
-      if (ncand <= 256) {
-        // compact the candidates in id order, then select among them
-        uint32_t* cand_key = scratch;
-        uint32_t* cand_id = scratch + 256;
-        uint32_t pos = 0;
-#pragma unroll
-        for (int32_t j = 0; j < nj; ++j) {
-          const uint32_t kj = key_at(j);
-          const bool c = kj >= lb;
-          const uint64_t m = __ballot(c);
-          if (c) {
-            const uint32_t r = pos + lanes_below(m);
-            cand_key[r] = kj;
-            cand_id[r] = (uint32_t)(j * 64 + lane);
-          }
-          pos += (uint32_t)__popcll(m);
-        }
-        wave_sync();
-        uint32_t ck[4], ci[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t i = (uint32_t)(j * 64 + lane);
-          ck[j] = i < ncand ? cand_key[i] : 0u;
-          ci[j] = i < ncand ? cand_id[i] : 0u;
-        }
-        wave_sync();  // the candidate area is reused for the selected set
-        uint32_t tg = 1u, T = 0u;
-        int32_t need_eq = 0;
-        if ((uint32_t)keff < ncand) threshold_search<4>(ck, (uint32_t)keff, tg, T, need_eq);
-        emit_selection<4>(ck, [&ci](int32_t j) { return ci[j]; }, keff, tg, T, need_eq, out_row,
-                         sel_key, sel_id);
-        done = true;
-      }
+      out_row[r] = (int32_t)sel_id[i];
     }
-    if (!done) {
-      uint32_t tg = 1u, T = 0u;
-      int32_t need_eq = 0;
-      if ((uint32_t)keff < nvalid)
-        threshold_radix<KPL>(key_at, nj, (uint32_t)keff, scratch, tg, T, need_eq);
-      if constexpr (KPL > 0) {
-        emit_selection<KPL>(kv, slot_id, keff, tg, T, need_eq, out_row, sel_key, sel_id);
-      } else {
-        // LDS-resident keys: the same emission, one slot at a time
-        const int32_t c_gt = keff - need_eq;
-        uint32_t pos_gt = 0, pos_eq = 0;
-#pragma unroll
-        for (int32_t j = 0; j < nj; ++j) {
-          const uint32_t kj = key_at(j);
-          const bool is_gt = kj >= tg && kj != 0u;
-          const bool is_eq = need_eq > 0 && kj == T && kj != 0u;
-          const uint64_t m_gt = __ballot(is_gt);
-          const uint64_t m_eq = __ballot(is_eq);
-          if (is_gt) {
-            const uint32_t r = pos_gt + lanes_below(m_gt);
-            sel_key[r] = kj;
-            sel_id[r] = (uint32_t)(j * 64 + lane);
-          }
-          if (is_eq) {
-            const uint32_t r = pos_eq + lanes_below(m_eq);
-            if (r < (uint32_t)need_eq) out_row[c_gt + (int32_t)r] = j * 64 + lane;
-          }
-          pos_gt += (uint32_t)__popcll(m_gt);
-          pos_eq += (uint32_t)__popcll(m_eq);
-        }
-        wave_sync();
-        for (int32_t i = lane; i < c_gt; i += 64) {
-          const uint32_t ki = sel_key[i];
-          int32_t r = 0;
-          for (int32_t j = 0; j < c_gt; ++j) {
-            const uint32_t kj = sel_key[j];
-            r += (kj > ki) || (kj == ki && j < i);
-          }
-          out_row[r] = (int32_t)sel_id[i];
-        }
-        wave_sync();
-      }
-    }
+    wave_sync();
   }
   for (int32_t j = keff + lane; j < k; j += 64) out_row[j] = -1;
 }
 
-// One wave finishes a row whose keys[0, nvb) hold the streamed block keys:
-// -inf up to nsel, pin, optional score write-back, select.  `wmem` is this
-// row's LDS state: keys (keys_words), then the select scratch.
-__device__ __forceinline__ void finish_row_wave(const Params& p, int64_t r, const RowGeom& g,
-                                                uint32_t* wmem) {
+// Selects row r whose block keys [0, g.nvb) sit in LDS `keys`.  WG: all nw
+// waves of the workgroup call this together (it holds workgroup barriers);
+// otherwise one wave calls it with nw == 1.  `ctl` (kCtlWords, with the
+// kCtlValid and kCtlCand counters zeroed before the caller's last barrier)
+// and `area` (16-byte aligned, max(kAreaMinWords, 2*kcap) words) are this
+// row's LDS scratch.  Also writes the optional fp32 score row.
+template <bool WG>
+__device__ __forceinline__ void select_row(const Params& p, int64_t r, const RowGeom& g,
+                                           uint32_t* keys, uint32_t* ctl, uint32_t* area,
+                                           int wave, int nw) {
   const int lane = threadIdx.x & 63;
-  uint32_t* keys = wmem;
-  for (int32_t b = g.nvb + lane; b < g.nsel; b += 64) keys[b] = kKeyNegInf;
-  wave_sync();
-  if (g.pin >= 0 && lane == 0) keys[g.pin] = kKeyPosInf;
-  wave_sync();
+  const int tid = wave * 64 + lane;
+  const int nt = nw * 64;
+  const int32_t nsel = g.nsel, k = p.k;
+  int32_t* out_row = p.out + r * p.ld_out;
+  uint64_t* cand = reinterpret_cast<uint64_t*>(area);
+
   if (p.scores) {
     float* srow = p.scores + r * p.ld_scores;
-    for (int32_t b = lane; b < p.nblocks; b += 64)
-      srow[b] = b < g.nsel ? key_value(keys[b]) : -__builtin_inff();
+    for (int32_t b = tid; b < p.nblocks; b += nt)
+      srow[b] = b < nsel ? key_value(block_key(keys, g, b)) : -__builtin_inff();
   }
-  uint32_t* scratch = wmem + p.keys_words;
-  int32_t* out_row = p.out + r * p.ld_out;
-  const int32_t n = g.nsel;
-  if (n <= 64) select_wave<1>(keys, n, p.k, p.kcap, out_row, scratch);
-  else if (n <= 128) select_wave<2>(keys, n, p.k, p.kcap, out_row, scratch);
-  else if (n <= 256) select_wave<4>(keys, n, p.k, p.kcap, out_row, scratch);
-  else if (n <= 512) select_wave<8>(keys, n, p.k, p.kcap, out_row, scratch);
-  else if (n <= 1024) select_wave<16>(keys, n, p.k, p.kcap, out_row, scratch);
-  else select_wave<0>(keys, n, p.k, p.kcap, out_row, scratch);
+
+  if (nsel <= 64) {
+    // One candidate per lane of wave 0: rank them all directly.
+    if (wave == 0) {
+      const uint32_t rk = lane < nsel ? rank_key(block_key(keys, g, lane)) : 0u;
+      const int32_t nvalid = (int32_t)__popcll(__ballot(rk != 0u));
+      const int32_t keff = k < nvalid ? k : nvalid;
+      cand[lane] = cand_word(rk, (uint32_t)lane);
+      wave_sync();
+      rank_candidates(cand, 64, keff, out_row, 0, 1);
+      for (int32_t j = keff + lane; j < k; j += 64) out_row[j] = -1;
+    }
+    return;
+  }
+
+  // (A) group maxima.  gpl group maxima per lane of wave 0 (64*gpl groups),
+  // chosen so that k stays at most half the groups where it can.
+  const int gpl = k <= 32 ? 1 : (k <= 64 ? 2 : 4);
+  const int32_t ng_max = 64 * gpl;
+  const int32_t na = nsel < nt ? nsel : nt;  // threads holding keys
+  int gl = 1;                                // lanes per group
+  while (gl * ng_max < na) gl <<= 1;
+  const int32_t ngroups = (na + gl - 1) / gl;
+  uint32_t tmax = 0u, nv = 0u;
+  for (int32_t base = wave * 64; base < nsel; base += nt) {  // wave-uniform
+    const int32_t i = base + lane;
+    const uint32_t rk = i < nsel ? rank_key(block_key(keys, g, i)) : 0u;
+    nv += (uint32_t)__popcll(__ballot(rk != 0u));
+    tmax = umax(tmax, rk);
+  }
+  if (wave * 64 < na) {
+    tmax = group_umax_dyn(tmax, gl);
+    if (tid < na && (tid & (gl - 1)) == 0) area[tid / gl] = tmax;
+  }
+  if (wave == 0) {
+    for (int32_t t = ngroups + lane; t < ng_max; t += 64) area[t] = 0u;
+  }
+  if (lane == 0 && nv != 0u) atomicAdd(&ctl[kCtlValid], nv);
+  row_barrier<WG>();
+
+  // (C) wave 0: T0 = the keff-th largest group maximum (at least 1).
+  if (wave == 0) {
+    const uint32_t nvalid = ctl[kCtlValid];
+    const int32_t keff = (uint32_t)k < nvalid ? k : (int32_t)nvalid;
+    uint32_t t0;
+    if (gpl == 1) {
+      // all-pairs count over the 64 maxima: c = #(m_j >= v); T0 = the largest
+      // v with c >= keff
+      const uint32_t v = area[lane];
+      const uint4* a4 = reinterpret_cast<const uint4*>(area);
+      uint32_t c = 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint4 m = a4[j];
+        c += (uint32_t)(m.x >= v) + (uint32_t)(m.y >= v) + (uint32_t)(m.z >= v) + (uint32_t)(m.w >= v);
+      }
+      t0 = group_umax<64>(c >= (uint32_t)keff ? v : 0u);
+    } else if (gpl == 2) {
+      const uint32_t kv[2] = {area[lane], area[64 + lane]};
+      t0 = kth_largest_search<2>(kv, (uint32_t)keff);
+    } else {
+      const uint32_t kv[4] = {area[lane], area[64 + lane], area[128 + lane], area[192 + lane]};
+      t0 = kth_largest_search<4>(kv, (uint32_t)keff);
+    }
+    if (lane == 0) {
+      ctl[kCtlT0] = t0 > 1u ? t0 : 1u;
+      ctl[kCtlKeff] = (uint32_t)keff;
+    }
+  }
+  row_barrier<WG>();
+
+  // (E) compact the candidates (keys >= T0) into LDS.
+  const uint32_t t0 = ctl[kCtlT0];
+  for (int32_t base = wave * 64; base < nsel; base += nt) {  // wave-uniform
+    const int32_t i = base + lane;
+    const uint32_t rk = i < nsel ? rank_key(block_key(keys, g, i)) : 0u;
+    const bool c = rk >= t0;
+    const uint64_t m = __ballot(c);
+    if (m != 0ull) {
+      uint32_t b0 = 0u;
+      if (lane == 0) b0 = atomicAdd(&ctl[kCtlCand], (uint32_t)__popcll(m));
+      b0 = (uint32_t)__builtin_amdgcn_readlane((int)b0, 0);
+      const uint32_t pos = b0 + lanes_below(m);
+      if (c && pos < (uint32_t)kCandCap) cand[pos] = cand_word(rk, (uint32_t)i);
+    }
+  }
+  row_barrier<WG>();
+
+  // (G) rank the candidates, or fall back to the exact one-wave select.
+  const int32_t ncand = (int32_t)ctl[kCtlCand];
+  const int32_t keff = (int32_t)ctl[kCtlKeff];
+  if (ncand <= kCandCap) {
+    rank_candidates(cand, ncand, keff, out_row, wave, nw);
+    for (int32_t j = keff + tid; j < k; j += nt) out_row[j] = -1;
+  } else if (wave == 0) {
+    for (int32_t b = g.nvb + lane; b < nsel; b += 64) keys[b] = kKeyNegInf;
+    wave_sync();
+    if (g.pin >= 0 && lane == 0) keys[g.pin] = kKeyPosInf;
+    wave_sync();
+    select_wave_exact(keys, nsel, k, p.kcap, out_row, area);
+  }
 }
 
 // Plan "wave": one wave per row, blockDim/64 rows per workgroup, no barrier.
-// U: float4 loads in flight per lane.
+// U: float4 loads in flight per lane.  Per-wave LDS: keys, ctl, area.
 template <int G, int U>
 __global__ void __launch_bounds__(kThreads) select_wave_rows_kernel(Params p) {
   extern __shared__ uint32_t smem[];
   const int wave = wave_index();
+  const int lane = threadIdx.x & 63;
   const int nw = blockDim.x >> 6;
-  uint32_t* wmem = smem + wave * p.wave_words;
+  uint32_t* keys = smem + wave * p.wave_words;
+  uint32_t* ctl = keys + p.keys_words;
+  uint32_t* area = ctl + kCtlWords;
   for (int64_t r = (int64_t)blockIdx.x * nw + wave; r < p.items; r += (int64_t)gridDim.x * nw) {
     const RowGeom g = row_geom(p, r, true);
-    stream_blocks<G, U>(p, g, 0, g.nvb, 0, 1, EmitKey{wmem});
+    if (lane < 4) ctl[lane] = 0u;
+    stream_blocks<G, U>(p, g, 0, g.nvb, 0, 1, EmitKey{keys});
     wave_sync();
-    finish_row_wave(p, r, g, wmem);
+    select_row<false>(p, r, g, keys, ctl, area, 0, 1);
     wave_sync();
   }
 }
 
-// Plan "group": all waves of a workgroup stream one row into LDS, wave 0
-// selects.
+// Plan "group": all waves of a workgroup stream one row into LDS, then select
+// it together.
 template <int G>
 __global__ void __launch_bounds__(1024) select_group_rows_kernel(Params p) {
   extern __shared__ uint32_t smem[];
   const int wave = wave_index();
   const int nw = blockDim.x >> 6;
+  uint32_t* ctl = smem + p.keys_words;
+  uint32_t* area = ctl + kCtlWords;
   for (int64_t r = blockIdx.x; r < p.items; r += gridDim.x) {
     const RowGeom g = row_geom(p, r, true);
+    if (threadIdx.x < 4) ctl[threadIdx.x] = 0u;
     stream_blocks<G, kUnroll>(p, g, 0, g.nvb, wave, nw, EmitKey{smem});
     __syncthreads();
-    if (wave == 0) finish_row_wave(p, r, g, smem);
+    select_row<true>(p, r, g, smem, ctl, area, wave, nw);
     if (r + gridDim.x < p.items) __syncthreads();  // LDS is reused by the next row
   }
 }
@@ -715,33 +702,35 @@ __global__ void __launch_bounds__(kThreads) stream_keys_kernel(Params p) {
   }
 }
 
-// Plan "split", second kernel: one wave per row reads the row's keys back
-// and selects.
-__global__ void __launch_bounds__(kThreads) select_keys_kernel(Params p) {
+// Plan "split", second kernel: one workgroup per row reads the row's keys
+// back into LDS and selects.
+__global__ void __launch_bounds__(1024) select_keys_kernel(Params p) {
   extern __shared__ uint32_t smem[];
   const int wave = wave_index();
-  const int lane = threadIdx.x & 63;
   const int nw = blockDim.x >> 6;
-  uint32_t* wmem = smem + wave * p.wave_words;
-  for (int64_t r = (int64_t)blockIdx.x * nw + wave; r < p.items; r += (int64_t)gridDim.x * nw) {
+  uint32_t* ctl = smem + p.keys_words;
+  uint32_t* area = ctl + kCtlWords;
+  for (int64_t r = blockIdx.x; r < p.items; r += gridDim.x) {
     const RowGeom g = row_geom(p, r, true);
+    if (threadIdx.x < 4) ctl[threadIdx.x] = 0u;
     const uint32_t* src = p.ws_keys + r * p.nblocks;
-    for (int32_t b0 = 0; b0 < g.nvb; b0 += 64 * 16) {  // 16 loads in flight per lane
-      uint32_t v[16];
+    const int32_t nt = (int32_t)blockDim.x;
+    for (int32_t b0 = 0; b0 < g.nvb; b0 += 4 * nt) {  // four loads in flight per lane
+      uint32_t v[4];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int32_t b = b0 + j * 64 + lane;
+      for (int j = 0; j < 4; ++j) {
+        const int32_t b = b0 + j * nt + (int32_t)threadIdx.x;
         v[j] = src[b < g.nvb ? b : g.nvb - 1];
       }
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int32_t b = b0 + j * 64 + lane;
-        if (b < g.nvb) wmem[b] = v[j];
+      for (int j = 0; j < 4; ++j) {
+        const int32_t b = b0 + j * nt + (int32_t)threadIdx.x;
+        if (b < g.nvb) smem[b] = v[j];
       }
     }
-    wave_sync();
-    finish_row_wave(p, r, g, wmem);
-    wave_sync();
+    __syncthreads();
+    select_row<true>(p, r, g, smem, ctl, area, wave, nw);
+    if (r + gridDim.x < p.items) __syncthreads();
   }
 }
 
@@ -848,14 +837,16 @@ int64_t select_kcap(int64_t nblocks, int32_t k) {
   return kc > 0 ? kc : 1;
 }
 
-// LDS words of one row's select state: keys, then a scratch that holds the
-// radix histogram (256 words) or the pruned candidates (2 x 256 words), and
-// later the selected keys and ids (2 x kcap); a multiple of 4 words.
+// LDS words of one row's select state: keys (nblocks rounded up to 4), the
+// control words, then an area for the group maxima, the candidates
+// (kCandCap 64-bit words) or, in the exact fallback, the radix histogram and
+// the selected keys and ids (2 x kcap); a multiple of 4 words.
 int64_t select_keys_words(int64_t nblocks) { return cdiv(nblocks, 4) * 4; }
 
 int64_t select_wave_words(int64_t nblocks, int32_t k) {
   const int64_t sel = 2 * select_kcap(nblocks, k);
-  return select_keys_words(nblocks) + cdiv(sel > 512 ? sel : 512, 4) * 4;
+  return select_keys_words(nblocks) + kCtlWords +
+         cdiv(sel > kAreaMinWords ? sel : kAreaMinWords, 4) * 4;
 }
 
 // Plan ids (also the values of dsa_select_candidate_blocks_plan's `plan`).
@@ -1044,8 +1035,11 @@ dsa_status_t dsa_select_candidate_blocks_plan(
   if (rows * (int64_t)p.nchunks > (int64_t)INT32_MAX) return DSA_ERR_UNSUPPORTED;
   dsa_status_t st = launch(stream_keys_kernel_ptr(g), rows * p.nchunks, kThreads, 1, 0, stream, p);
   if (st != DSA_OK) return st;
-  return launch(reinterpret_cast<void*>(&select_keys_kernel), rows, 64 * (int)nw, (int)nw,
-                wave_lds, stream, p);
+  // one workgroup per row, one key per thread up to 1024 keys
+  int64_t sel_waves = cdiv(nblocks, 64);
+  if (sel_waves > 16) sel_waves = 16;
+  return launch(reinterpret_cast<void*>(&select_keys_kernel), rows, 64 * (int)sel_waves, 1,
+                (size_t)ww * 4, stream, p);
 }
 
 dsa_status_t dsa_select_candidate_blocks(const float* logits, int64_t rows, int64_t width,
