@@ -103,9 +103,9 @@ size_t dsa_select_workspace_bytes(int64_t rows, int64_t width, int32_t block_siz
  *               pinned block scores, for checking; ld_scores is ignored when
  *               scores_out is NULL.
  *   workspace   device scratch for the split plan (few long rows): at least
- *               dsa_select_workspace_bytes(...) bytes, 4-byte aligned, no
- *               initialisation needed.  Other plans do not touch it and it
- *               may then be NULL (dsa_select_plan tells the plan).  Calls
+ *               dsa_select_workspace_bytes(...) bytes, 4-byte aligned,
+ *               no initialisation needed.  Other plans do not touch it and
+ *               it may then be NULL (dsa_select_plan tells the plan).  Calls
  *               that may run concurrently need separate workspaces.
  *
  * rows == 0 or topk_blocks == 0: DSA_OK, nothing written.
@@ -116,7 +116,7 @@ size_t dsa_select_workspace_bytes(int64_t rows, int64_t width, int32_t block_siz
  *   ld_logits < width, ld_out < topk_blocks, ld_scores < nblocks when
  *   scores_out is given, null logits/row_ke/out when there is work,
  *   misaligned pointers.
- * Unsupported: 4 * (roundup4(nblocks) + 32 + roundup4(max(512, 2*kcap))) > 65536
+ * Unsupported: 4 * (roundup4(nblocks) + 16 + roundup4(max(512, 2*kcap))) > 65536
  *   with kcap = max(1, min(topk_blocks, nblocks)) (a row's block scores and
  *   select scratch must fit in LDS), or more than 2^31 - 1 rows.
  */

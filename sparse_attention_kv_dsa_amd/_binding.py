@@ -121,11 +121,11 @@ class Workspace:
 
     def __init__(self, device, nbytes: int = 0):
         self.device = torch.device(device)
-        self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
 
     def ensure(self, nbytes: int) -> "Workspace":
         if nbytes > self.buf.numel():
-            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
         return self
 
 

@@ -302,12 +302,11 @@ struct EmitScore {
 // More than kCandCap candidates (heavy ties at T0, or k in the hundreds)
 // fall back to an exact one-wave radix select over the LDS keys.
 
-constexpr int kCtlWords = 32;   // per-row control words in LDS
-constexpr int kCtlValid = 0;    // #nonzero rank keys (atomic)
-constexpr int kCtlCand = 1;     // #candidates (atomic)
-constexpr int kCtlT0 = 2;       // candidate threshold
-constexpr int kCtlKeff = 3;     // min(k, #nonzero)
-constexpr int kCandCap = 256;   // candidates held in LDS
+constexpr int kCtlWords = 16;   // per-row control words in LDS
+constexpr int kCtlValid = 0;    // #nonzero rank keys (atomic add)
+constexpr int kCtlCand = 1;     // #candidates (atomic add)
+constexpr int kCtlT0 = 2;       // candidate threshold (atomic max)
+constexpr int kCandCap = 256;   // candidates held in LDS (64-bit words)
 constexpr int kAreaMinWords = 2 * kCandCap;
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
@@ -350,7 +349,8 @@ __device__ __forceinline__ void row_barrier() {
 
 // Score key of block i < nsel of a row whose blocks [0, nvb) sit in keys[].
 __device__ __forceinline__ uint32_t block_key(const uint32_t* keys, const RowGeom& g, int32_t i) {
-  return i == g.pin ? kKeyPosInf : (i < g.nvb ? keys[i] : kKeyNegInf);
+  const uint32_t raw = keys[i < g.nvb ? i : 0];  // keys[0] is in bounds; masked below
+  return i == g.pin ? kKeyPosInf : (i < g.nvb ? raw : kKeyNegInf);
 }
 
 // Candidate word: rank key above, inverted id below; 0 for a non-candidate.
@@ -519,119 +519,98 @@ __device__ void select_wave_exact(const uint32_t* keys, int32_t nsel, int32_t k,
   for (int32_t j = keff + lane; j < k; j += 64) out_row[j] = -1;
 }
 
-// Selects row r whose block keys [0, g.nvb) sit in LDS `keys`.  WG: all nw
-// waves of the workgroup call this together (it holds workgroup barriers);
-// otherwise one wave calls it with nw == 1.  `ctl` (kCtlWords, with the
-// kCtlValid and kCtlCand counters zeroed before the caller's last barrier)
-// and `area` (16-byte aligned, max(kAreaMinWords, 2*kcap) words) are this
-// row's LDS scratch.  Also writes the optional fp32 score row.
-template <bool WG>
-__device__ __forceinline__ void select_row(const Params& p, int64_t r, const RowGeom& g,
-                                           uint32_t* keys, uint32_t* ctl, uint32_t* area,
-                                           int wave, int nw) {
+// Rank key of block i for the select; 0 for i >= nsel.  The LDS read is
+// unconditional (clamped to a valid index) so the code stays branch-free.
+__device__ __forceinline__ uint32_t select_rank_key(const uint32_t* keys, const RowGeom& g,
+                                                    int32_t i) {
+  const uint32_t raw = keys[i < g.nvb ? i : 0];
+  uint32_t key = i < g.nvb ? raw : kKeyNegInf;
+  key = i == g.pin ? kKeyPosInf : key;
+  return i < g.nsel ? rank_key(key) : 0u;
+}
+
+// Clears the LDS state select_row expects zeroed: the group maxima (the first
+// 256 words of `area`) and the control counters.  Call before the barrier
+// that precedes select_row (the streaming never touches these words).
+__device__ __forceinline__ void select_row_prepare(uint32_t* ctl, uint32_t* area, int tid, int nt) {
+  for (int t = tid; t < 256; t += nt) area[t] = 0u;
+  if (tid < kCtlWords) ctl[tid] = 0u;
+}
+
+// The general path of select_row (nsel > 64) with NGM = 64*GPL groups; group
+// of key i = i mod NGM (a group's maximum is an LDS atomic max).
+template <bool WG, int GPL>
+__device__ __forceinline__ void select_row_general(const Params& p, const RowGeom& g,
+                                                   uint32_t* keys, uint32_t* ctl, uint32_t* area,
+                                                   int32_t* out_row, int wave, int nw) {
+  constexpr int NGM = 64 * GPL;
   const int lane = threadIdx.x & 63;
   const int tid = wave * 64 + lane;
   const int nt = nw * 64;
   const int32_t nsel = g.nsel, k = p.k;
-  int32_t* out_row = p.out + r * p.ld_out;
+  uint32_t* gm = area;
   uint64_t* cand = reinterpret_cast<uint64_t*>(area);
 
-  if (p.scores) {
-    float* srow = p.scores + r * p.ld_scores;
-    for (int32_t b = tid; b < p.nblocks; b += nt)
-      srow[b] = b < nsel ? key_value(block_key(keys, g, b)) : -__builtin_inff();
-  }
-
-  if (nsel <= 64) {
-    // One candidate per lane of wave 0: rank them all directly.
-    if (wave == 0) {
-      const uint32_t rk = lane < nsel ? rank_key(block_key(keys, g, lane)) : 0u;
-      const int32_t nvalid = (int32_t)__popcll(__ballot(rk != 0u));
-      const int32_t keff = k < nvalid ? k : nvalid;
-      cand[lane] = cand_word(rk, (uint32_t)lane);
-      wave_sync();
-      rank_candidates(cand, 64, keff, out_row, 0, 1);
-      for (int32_t j = keff + lane; j < k; j += 64) out_row[j] = -1;
-    }
-    return;
-  }
-
-  // (A) group maxima.  gpl group maxima per lane of wave 0 (64*gpl groups),
-  // chosen so that k stays at most half the groups where it can.
-  const int gpl = k <= 32 ? 1 : (k <= 64 ? 2 : 4);
-  const int32_t ng_max = 64 * gpl;
-  const int32_t na = nsel < nt ? nsel : nt;  // threads holding keys
-  int gl = 1;                                // lanes per group
-  while (gl * ng_max < na) gl <<= 1;
-  const int32_t ngroups = (na + gl - 1) / gl;
-  uint32_t tmax = 0u, nv = 0u;
+  // (A) group maxima and the count of nonzero rank keys.
+  uint32_t nv = 0u;
   for (int32_t base = wave * 64; base < nsel; base += nt) {  // wave-uniform
     const int32_t i = base + lane;
-    const uint32_t rk = i < nsel ? rank_key(block_key(keys, g, i)) : 0u;
+    const uint32_t rk = select_rank_key(keys, g, i);
+    if (rk != 0u) atomicMax(&gm[i & (NGM - 1)], rk);
     nv += (uint32_t)__popcll(__ballot(rk != 0u));
-    tmax = umax(tmax, rk);
-  }
-  if (wave * 64 < na) {
-    tmax = group_umax_dyn(tmax, gl);
-    if (tid < na && (tid & (gl - 1)) == 0) area[tid / gl] = tmax;
-  }
-  if (wave == 0) {
-    for (int32_t t = ngroups + lane; t < ng_max; t += 64) area[t] = 0u;
   }
   if (lane == 0 && nv != 0u) atomicAdd(&ctl[kCtlValid], nv);
   row_barrier<WG>();
 
-  // (C) wave 0: T0 = the keff-th largest group maximum (at least 1).
-  if (wave == 0) {
-    const uint32_t nvalid = ctl[kCtlValid];
-    const int32_t keff = (uint32_t)k < nvalid ? k : (int32_t)nvalid;
-    uint32_t t0;
-    if (gpl == 1) {
-      // all-pairs count over the 64 maxima: c = #(m_j >= v); T0 = the largest
-      // v with c >= keff
-      const uint32_t v = area[lane];
-      const uint4* a4 = reinterpret_cast<const uint4*>(area);
-      uint32_t c = 0;
+  // (C) keff = min(k, #nonzero); T0 = the keff-th largest group maximum.
+  // Wave w tests a slice of the maxima: v qualifies when #(maxima >= v) >=
+  // keff (one ballot per slot); the largest qualifying v goes to ctl[kCtlT0].
+  const uint32_t nvalid = ctl[kCtlValid];
+  const int32_t keff = (uint32_t)k < nvalid ? k : (int32_t)nvalid;
+  {
+    uint32_t gv[GPL];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint4 m = a4[j];
-        c += (uint32_t)(m.x >= v) + (uint32_t)(m.y >= v) + (uint32_t)(m.z >= v) + (uint32_t)(m.w >= v);
-      }
-      t0 = group_umax<64>(c >= (uint32_t)keff ? v : 0u);
-    } else if (gpl == 2) {
-      const uint32_t kv[2] = {area[lane], area[64 + lane]};
-      t0 = kth_largest_search<2>(kv, (uint32_t)keff);
-    } else {
-      const uint32_t kv[4] = {area[lane], area[64 + lane], area[128 + lane], area[192 + lane]};
-      t0 = kth_largest_search<4>(kv, (uint32_t)keff);
+    for (int s = 0; s < GPL; ++s) gv[s] = gm[s * 64 + lane];
+    const int32_t len = (NGM + nw - 1) / nw;
+    const int32_t l0 = wave * len;
+    const int32_t l1 = l0 + len < NGM ? l0 + len : NGM;
+    uint32_t best = 0u;
+    for (int32_t l = l0; l < l1; ++l) {  // wave-uniform
+      uint32_t src = gv[0];
+#pragma unroll
+      for (int s = 1; s < GPL; ++s) src = (l >> 6) == s ? gv[s] : src;
+      const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)src, l & 63);
+      uint32_t c = 0u;
+#pragma unroll
+      for (int s = 0; s < GPL; ++s) c += (uint32_t)__popcll(__ballot(gv[s] >= v));
+      best = (c >= (uint32_t)keff && v > best) ? v : best;
     }
-    if (lane == 0) {
-      ctl[kCtlT0] = t0 > 1u ? t0 : 1u;
-      ctl[kCtlKeff] = (uint32_t)keff;
-    }
+    if (lane == 0 && best != 0u) atomicMax(&ctl[kCtlT0], best);
   }
   row_barrier<WG>();
 
   // (E) compact the candidates (keys >= T0) into LDS.
-  const uint32_t t0 = ctl[kCtlT0];
-  for (int32_t base = wave * 64; base < nsel; base += nt) {  // wave-uniform
-    const int32_t i = base + lane;
-    const uint32_t rk = i < nsel ? rank_key(block_key(keys, g, i)) : 0u;
-    const bool c = rk >= t0;
-    const uint64_t m = __ballot(c);
-    if (m != 0ull) {
-      uint32_t b0 = 0u;
-      if (lane == 0) b0 = atomicAdd(&ctl[kCtlCand], (uint32_t)__popcll(m));
-      b0 = (uint32_t)__builtin_amdgcn_readlane((int)b0, 0);
-      const uint32_t pos = b0 + lanes_below(m);
-      if (c && pos < (uint32_t)kCandCap) cand[pos] = cand_word(rk, (uint32_t)i);
+  {
+    const uint32_t t0r = ctl[kCtlT0];
+    const uint32_t t0 = t0r > 1u ? t0r : 1u;
+    for (int32_t base = wave * 64; base < nsel; base += nt) {  // wave-uniform
+      const int32_t i = base + lane;
+      const uint32_t rk = select_rank_key(keys, g, i);
+      const bool c = rk >= t0;
+      const uint64_t m = __ballot(c);
+      if (m != 0ull) {
+        uint32_t b0 = 0u;
+        if (lane == 0) b0 = atomicAdd(&ctl[kCtlCand], (uint32_t)__popcll(m));
+        b0 = (uint32_t)__builtin_amdgcn_readlane((int)b0, 0);
+        const uint32_t pos = b0 + lanes_below(m);
+        if (c && pos < (uint32_t)kCandCap) cand[pos] = cand_word(rk, (uint32_t)i);
+      }
     }
   }
   row_barrier<WG>();
 
   // (G) rank the candidates, or fall back to the exact one-wave select.
   const int32_t ncand = (int32_t)ctl[kCtlCand];
-  const int32_t keff = (int32_t)ctl[kCtlKeff];
   if (ncand <= kCandCap) {
     rank_candidates(cand, ncand, keff, out_row, wave, nw);
     for (int32_t j = keff + tid; j < k; j += nt) out_row[j] = -1;
@@ -644,20 +623,60 @@ __device__ __forceinline__ void select_row(const Params& p, int64_t r, const Row
   }
 }
 
+// Selects row r whose block keys [0, g.nvb) sit in LDS `keys`.  WG: all nw
+// waves of the workgroup call this together (it holds workgroup barriers);
+// otherwise one wave calls it with nw == 1.  `ctl` (kCtlWords) and `area`
+// (16-byte aligned, max(kAreaMinWords, 2*kcap) words) are this row's LDS
+// scratch, cleared by select_row_prepare before the caller's last barrier.
+// Also writes the optional fp32 score row.
+template <bool WG>
+__device__ __forceinline__ void select_row(const Params& p, int64_t r, const RowGeom& g,
+                                           uint32_t* keys, uint32_t* ctl, uint32_t* area,
+                                           int wave, int nw) {
+  const int lane = threadIdx.x & 63;
+  const int tid = wave * 64 + lane;
+  const int nt = nw * 64;
+  const int32_t nsel = g.nsel, k = p.k;
+  int32_t* out_row = p.out + r * p.ld_out;
+
+  if (p.scores) {
+    float* srow = p.scores + r * p.ld_scores;
+    for (int32_t b = tid; b < p.nblocks; b += nt)
+      srow[b] = b < nsel ? key_value(block_key(keys, g, b)) : -__builtin_inff();
+  }
+
+  if (nsel <= 64) {
+    // One candidate per lane of wave 0: rank them all directly.
+    if (wave == 0) {
+      uint64_t* cand = reinterpret_cast<uint64_t*>(area);
+      const uint32_t rk = select_rank_key(keys, g, lane);
+      const int32_t nvalid = (int32_t)__popcll(__ballot(rk != 0u));
+      const int32_t keff = k < nvalid ? k : nvalid;
+      cand[lane] = cand_word(rk, (uint32_t)lane);
+      wave_sync();
+      rank_candidates(cand, 64, keff, out_row, 0, 1);
+      for (int32_t j = keff + lane; j < k; j += 64) out_row[j] = -1;
+    }
+    return;
+  }
+  if (k <= 32) select_row_general<WG, 1>(p, g, keys, ctl, area, out_row, wave, nw);
+  else if (k <= 64) select_row_general<WG, 2>(p, g, keys, ctl, area, out_row, wave, nw);
+  else select_row_general<WG, 4>(p, g, keys, ctl, area, out_row, wave, nw);
+}
+
 // Plan "wave": one wave per row, blockDim/64 rows per workgroup, no barrier.
 // U: float4 loads in flight per lane.  Per-wave LDS: keys, ctl, area.
 template <int G, int U>
 __global__ void __launch_bounds__(kThreads) select_wave_rows_kernel(Params p) {
   extern __shared__ uint32_t smem[];
   const int wave = wave_index();
-  const int lane = threadIdx.x & 63;
   const int nw = blockDim.x >> 6;
   uint32_t* keys = smem + wave * p.wave_words;
   uint32_t* ctl = keys + p.keys_words;
   uint32_t* area = ctl + kCtlWords;
   for (int64_t r = (int64_t)blockIdx.x * nw + wave; r < p.items; r += (int64_t)gridDim.x * nw) {
     const RowGeom g = row_geom(p, r, true);
-    if (lane < 4) ctl[lane] = 0u;
+    select_row_prepare(ctl, area, threadIdx.x & 63, 64);
     stream_blocks<G, U>(p, g, 0, g.nvb, 0, 1, EmitKey{keys});
     wave_sync();
     select_row<false>(p, r, g, keys, ctl, area, 0, 1);
@@ -676,7 +695,7 @@ __global__ void __launch_bounds__(1024) select_group_rows_kernel(Params p) {
   uint32_t* area = ctl + kCtlWords;
   for (int64_t r = blockIdx.x; r < p.items; r += gridDim.x) {
     const RowGeom g = row_geom(p, r, true);
-    if (threadIdx.x < 4) ctl[threadIdx.x] = 0u;
+    select_row_prepare(ctl, area, threadIdx.x, blockDim.x);
     stream_blocks<G, kUnroll>(p, g, 0, g.nvb, wave, nw, EmitKey{smem});
     __syncthreads();
     select_row<true>(p, r, g, smem, ctl, area, wave, nw);
@@ -712,7 +731,7 @@ __global__ void __launch_bounds__(1024) select_keys_kernel(Params p) {
   uint32_t* area = ctl + kCtlWords;
   for (int64_t r = blockIdx.x; r < p.items; r += gridDim.x) {
     const RowGeom g = row_geom(p, r, true);
-    if (threadIdx.x < 4) ctl[threadIdx.x] = 0u;
+    select_row_prepare(ctl, area, threadIdx.x, blockDim.x);
     const uint32_t* src = p.ws_keys + r * p.nblocks;
     const int32_t nt = (int32_t)blockDim.x;
     for (int32_t b0 = 0; b0 < g.nvb; b0 += 4 * nt) {  // four loads in flight per lane
@@ -852,12 +871,12 @@ int64_t select_wave_words(int64_t nblocks, int32_t k) {
 // Plan ids (also the values of dsa_select_candidate_blocks_plan's `plan`).
 enum { kPlanGroup = 1, kPlanSplit = 2, kPlanWave = 3 };
 
-// Chunk size for split rows: aim at ~2048 workgroups in total, 2K-16K columns
+// Chunk size for split rows: aim at ~2048 workgroups in total, 8K-32K columns
 // each, and a multiple of the blocks one wave instruction covers.
 int32_t auto_chunk_blocks(int64_t rows, int64_t width, int32_t B) {
   int64_t cols = rows > 0 ? (rows * width) / 2048 : width;
-  if (cols < 2048) cols = 2048;
-  if (cols > 16384) cols = 16384;
+  if (cols < 8192) cols = 8192;
+  if (cols > 32768) cols = 32768;
   int64_t cb = cdiv(cols, B);
   const int g = lanes_per_block(B);
   if (g > 0) {
@@ -904,13 +923,16 @@ dsa_status_t dsa_select_plan(int64_t rows, int64_t width, int32_t block_size,
     // each, long rows a whole workgroup each.
     *plan = width <= 16384 ? kPlanWave : kPlanGroup;
     if (*plan == kPlanGroup) *plan_arg = kWaves;
-  } else if (rows >= 64) {
-    // Decode batches: one CU per row with up to 16 waves streaming it, the
-    // select fused behind them (a single launch; measured faster than the
-    // split plan's two kernels down to 64 rows).
+  } else if (rows >= 64 && width < 65536) {
+    // Decode batches of rows up to 256 KiB: one CU per row with up to 16
+    // waves streaming it, the select fused behind them (a single launch;
+    // measured faster than the split plan's two kernels for such rows).
     *plan = kPlanGroup;
     *plan_arg = rows <= 256 ? 16 : (rows <= 512 ? 8 : kWaves);
   } else {
+    // Few rows, or long rows: chunks of every row on all CUs, then a
+    // selecting kernel (one CU streams only ~25-70 GB/s, so a row per CU
+    // cannot keep HBM busy).
     *plan = kPlanSplit;
     *plan_arg = cb;
   }

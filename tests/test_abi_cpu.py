@@ -65,8 +65,9 @@ def test_auto_plan():
     assert B.select_plan(8192, 65536, 64, 64) == (1, 4)    # many long rows: a workgroup per row
     assert B.select_plan(8, 1000, 64, 4) == (3, 0)         # one chunk per row anyway
     assert B.select_plan(64, 32768, 64, 32) == (1, 16)     # decode: a 16-wave CU per row
-    assert B.select_plan(128, 131072, 128, 16) == (1, 16)
-    assert B.select_plan(600, 131072, 128, 16) == (1, 4)
+    assert B.select_plan(128, 131072, 128, 16) == (2, 64)  # long decode rows: 32 KiB chunks
+    assert B.select_plan(600, 131072, 128, 16) == (2, 256)  # 128 KiB chunks
+    assert B.select_plan(600, 32768, 64, 32) == (1, 4)
     p, cb = B.select_plan(16, 131072, 128, 16)             # very few long rows: split
     assert p == 2 and cb % 2 == 0 and cb >= 1
 
@@ -91,8 +92,8 @@ def _sel(**kw):
     (dict(ws=None, plan=2), 3), (dict(ws_bytes=100, plan=2), 3), (dict(ws=FAKE + 2, plan=2), 3),
     (dict(ws=None, plan=2, cb=3), 3),
     (dict(width=1 << 20, ld=1 << 20, B=16, k=4096, ld_out=4096), 2),  # keys do not fit in LDS
-    (dict(width=15840 * 4 + 4, ld=1 << 16, B=4, k=3, ld_out=3), 2),   # 15844 + 32 + 512 words > 16384
-    (dict(width=15840 * 4, ld=1 << 16, B=4, k=3, ld_out=3, plan=2, ws=None), 3),  # 15840 + 32 + 512 fits
+    (dict(width=15856 * 4 + 4, ld=1 << 16, B=4, k=3, ld_out=3), 2),   # 15860 + 16 + 512 words > 16384
+    (dict(width=15856 * 4, ld=1 << 16, B=4, k=3, ld_out=3, plan=2, ws=None), 3),  # 15856 + 16 + 512 fits
     (dict(rows=0), 0), (dict(k=0), 0), (dict(rows=0, logits=None, ke=None, out=None), 0),
 ])
 def test_select_rejects_on_host(kw, code):
