@@ -8,7 +8,9 @@ The arithmetic lives in ``oracle.c`` (plain loops, one qsort per row); this
 module compiles it with gcc and marshals numpy arrays through ctypes.  The
 definition it implements is stated at the top of ``oracle.c`` and follows
 the vLLM-fork page ``candidate_blocks.py`` (functions ``_max_with_nan``,
-``_block_scores_kernel``, ``_block_scores``, ``_select_candidate_blocks_impl``).
+``_block_scores_kernel``, ``_block_scores``, ``_select_candidate_blocks_impl``
+with its DCP branch, and the masking function after it) and page 3
+(``_correct_attn_cp_out_kernel`` / ``correct_attn_out``).
 """
 from __future__ import annotations
 
@@ -45,6 +47,13 @@ def _open(path):
     lib.oracle_select_candidate_blocks.argtypes = [vp, i64, i64, i64, vp, vp, i32, i32,
                                                    i32, vp, i64, vp, i64, ctypes.c_int]
     lib.oracle_select_candidate_blocks.restype = ctypes.c_int
+    lib.oracle_select_from_scores.argtypes = [vp, i64, i64, i64, i64, vp, i32, i32, i32, vp, i64]
+    lib.oracle_select_from_scores.restype = ctypes.c_int
+    lib.oracle_mask_candidates.argtypes = [vp, i64, i64, i64, vp, vp, vp, i64, i32, i32, i32]
+    lib.oracle_mask_candidates.restype = ctypes.c_int
+    lib.oracle_correct_attn_out.argtypes = ([vp] + [i64] * 6 + [vp] + [i64] * 5 + [vp] + [i64] * 3
+                                            + [vp, i64, i64])
+    lib.oracle_correct_attn_out.restype = ctypes.c_int
     return lib
 
 
@@ -88,7 +97,8 @@ def _ld(a):
     """Row stride in elements (an empty or one-row array may report any stride)."""
     if a.shape[0] <= 1 or a.shape[1] == 0:
         return max(int(a.shape[1]), 1)
-    assert a.strides[1] == a.itemsize and a.strides[0] % a.itemsize == 0
+    # a one-column array may report any column stride
+    assert (a.shape[1] == 1 or a.strides[1] == a.itemsize) and a.strides[0] % a.itemsize == 0
     return a.strides[0] // a.itemsize
 
 
@@ -137,3 +147,60 @@ def select_candidate_blocks(logits: np.ndarray, row_ks, row_ke, topk_blocks: int
         topk_blocks, block_size, row_repeat, _ptr(out), _ld(out),
         _ptr(scores_out), ld_scores, nthreads)
     assert rc == 0
+
+
+def select_from_scores(scores: np.ndarray, global_row_ke, topk_blocks: int,
+                       global_block_size: int, max_global_blocks: int, out: np.ndarray,
+                       row_repeat: int = 1) -> None:
+    """DCP branch after the reduce: pin from the global ends (clamped), rows with
+    end <= 0 select nothing, then the ordered -1 padded top-k.  ``scores`` is
+    fp32 [rows, nscore]; columns past ``max_global_blocks`` are dropped and
+    missing ones are -inf."""
+    assert scores.dtype == np.float32 and scores.ndim == 2
+    rows, nscore = scores.shape
+    ends = np.ascontiguousarray(global_row_ke, dtype=np.int32).reshape(-1)
+    assert ends.size >= (-(-rows // row_repeat) if rows else 0)
+    assert out.dtype == np.int32 and out.shape[0] == rows and out.shape[1] >= topk_blocks
+    ld = _ld(scores) if nscore else 1
+    rc = _load().oracle_select_from_scores(_ptr(scores), rows, nscore, ld, max_global_blocks,
+                                           _ptr(ends), row_repeat, global_block_size,
+                                           topk_blocks, _ptr(out), _ld(out))
+    assert rc == 0
+
+
+def mask_candidates(logits: np.ndarray, row_ks, row_ke, candidates: np.ndarray,
+                    topk_blocks: int, block_size: int, row_repeat: int = 1) -> None:
+    """In place: every column outside [s, e) or whose request-local block is
+    not among ``candidates[r, :topk_blocks]`` becomes -inf."""
+    row_ks, row_ke = _check_inputs(logits, row_ks, row_ke, row_repeat)
+    rows, width = logits.shape
+    assert candidates.dtype == np.int32 and candidates.shape[0] == rows
+    assert candidates.shape[1] >= topk_blocks
+    if rows and width:
+        rc = _load().oracle_mask_candidates(_ptr(logits), rows, width, _ld(logits),
+                                            _ptr(row_ks), _ptr(row_ke), _ptr(candidates),
+                                            _ld(candidates), topk_blocks, block_size,
+                                            row_repeat)
+        assert rc == 0
+
+
+def correct_attn_out(out: np.ndarray, lses: np.ndarray, cp_rank: int):
+    """Base-2 LSE correction: returns (new_out [H, B, D], lse [B, H]) in float64
+    for fp32 ``out [B, H, D]`` and ``lses [N, B, H]`` (any strides)."""
+    assert out.dtype == np.float32 and out.ndim == 3
+    assert lses.dtype == np.float32 and lses.ndim == 3
+    B, H, D = out.shape
+    N = lses.shape[0]
+    assert lses.shape[1:] == (B, H) and 0 <= cp_rank < N
+    new = np.empty((H, B, D), dtype=np.float64)
+    lse = np.empty((B, H), dtype=np.float64)
+    isz = out.itemsize
+    o = [st // isz for st in out.strides]
+    l = [st // lses.itemsize for st in lses.strides]
+    n = [st // 8 for st in new.strides]
+    v = [st // 8 for st in lse.strides]
+    rc = _load().oracle_correct_attn_out(_ptr(out), B, H, D, o[0], o[1], o[2], _ptr(lses), N,
+                                         l[0], l[1], l[2], cp_rank, _ptr(new), n[0], n[1],
+                                         n[2], _ptr(lse), v[0], v[1])
+    assert rc == 0
+    return new, lse

@@ -31,6 +31,12 @@
  * so no rounding occurs anywhere; the oracle compares the fp32 values as
  * they are.
  *
+ * Also defined below, each with its source: the selection from a reduced
+ * block-score matrix under decode context parallelism (oracle_select_from_
+ * scores), the candidate masking of packed logits (oracle_mask_candidates)
+ * and the base-2 log-sum-exp correction of partial attention outputs
+ * (oracle_correct_attn_out, page 3).
+ *
  * Parity status: block scores, pin and the ordered select are pinned by the
  * hand-worked rows, the brute-force full sort, the B=1, torch.topk and
  * column-interleave decompositions in tests/.  The NaN placement in the
@@ -254,4 +260,147 @@ int oracle_select_candidate_blocks(const float* logits, int64_t rows, int64_t wi
   j.scores_out = scores_out;
   j.ld_scores = ld_scores;
   return run_rows(j, nthreads);
+}
+
+/* ------------------------------------------------------------------------
+ * Selection from a block-score matrix under decode context parallelism.
+ *
+ * Source: the same page, _select_candidate_blocks_impl, DCP branch.  Each
+ * rank scores its interleaved share of the columns at the local block size
+ * with the pin off; the element-wise maximum over ranks gives the global
+ * block scores (one all-reduce); every rank then pins and selects from the
+ * global bounds.  This function is the part after the reduce:
+ *   nblocks = max(max_global_blocks, 1);
+ *   full[b] = scores[r][b] for b < min(nscore, nblocks), else -inf;
+ *   e = global_ends[r div R];
+ *   p = clamp(floor((e - 1) / G), 0, nblocks - 1); full[p] = +inf;
+ *   if e <= 0 every full[b] = -inf (rows without context select nothing);
+ *   then the ranking and the -1 padded output of the non-DCP branch, with
+ *   k' = min(k, nblocks).
+ * The clamp (rather than skipping a pin past the last block) and the pin
+ * from the global end alone (no start) are the page's.
+ */
+static int64_t floor_div(int64_t a, int64_t b) {
+  int64_t q = a / b;
+  if ((a % b != 0) && ((a < 0) != (b < 0))) --q;
+  return q;
+}
+
+int oracle_select_from_scores(const float* scores, int64_t rows, int64_t nscore,
+                              int64_t ld_scores, int64_t max_global_blocks,
+                              const int32_t* global_ends, int32_t row_repeat,
+                              int32_t global_block_size, int32_t topk, int32_t* out,
+                              int64_t ld_out) {
+  if (rows <= 0) return 0;
+  int64_t nblocks = max_global_blocks > 1 ? max_global_blocks : 1;
+  int64_t kk = topk < nblocks ? topk : nblocks;
+  float* full = (float*)malloc(sizeof(float) * (size_t)nblocks);
+  ranked_t* order = (ranked_t*)malloc(sizeof(ranked_t) * (size_t)nblocks);
+  if (!full || !order) {
+    free(full);
+    free(order);
+    return 1;
+  }
+  int64_t ncopy = nscore < nblocks ? nscore : nblocks;
+  for (int64_t r = 0; r < rows; ++r) {
+    int64_t e = (int64_t)global_ends[r / row_repeat];
+    for (int64_t b = 0; b < nblocks; ++b)
+      full[b] = b < ncopy ? scores[r * ld_scores + b] : -INFINITY;
+    int64_t p = floor_div(e - 1, global_block_size);
+    if (p < 0) p = 0;
+    if (p > nblocks - 1) p = nblocks - 1;
+    full[p] = INFINITY;
+    if (e <= 0)
+      for (int64_t b = 0; b < nblocks; ++b) full[b] = -INFINITY;
+    for (int64_t b = 0; b < nblocks; ++b) {
+      order[b].score = full[b];
+      order[b].id = (int32_t)b;
+    }
+    qsort(order, (size_t)nblocks, sizeof(ranked_t), rank_cmp);
+    int32_t* o = out + r * ld_out;
+    for (int64_t q = 0; q < topk; ++q) {
+      const int minus_inf = isinf(order[q].score) && order[q].score < 0;
+      o[q] = (q < kk && !minus_inf) ? order[q].id : -1;
+    }
+  }
+  free(full);
+  free(order);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Candidate masking of packed logits (the step after selection).
+ *
+ * Source: the same page, the masking function whose docstring says it masks
+ * packed logits outside the causal bounds and outside the request-local
+ * candidates (its name and body are not shown).  Reading taken: for row r
+ * with bounds s, e (g = r div R), column c < width keeps its value when
+ * s <= c < e and its request-local block (c - s) div B is one of
+ * cand[r][0 .. topk) (entries < 0 match nothing); every other column becomes
+ * -inf.  In place.
+ */
+int oracle_mask_candidates(float* logits, int64_t rows, int64_t width, int64_t ld,
+                           const int32_t* starts, const int32_t* ends, const int32_t* cand,
+                           int64_t ld_cand, int32_t topk, int32_t block_size,
+                           int32_t row_repeat) {
+  for (int64_t r = 0; r < rows; ++r) {
+    int64_t s, e;
+    row_bounds(r, starts, ends, row_repeat, &s, &e);
+    const int32_t* cr = cand + r * ld_cand;
+    float* row = logits + r * ld;
+    for (int64_t c = 0; c < width; ++c) {
+      int keep = 0;
+      if (c >= s && c < e) {
+        int64_t b = (c - s) / block_size;
+        for (int32_t j = 0; j < topk && !keep; ++j) keep = cr[j] >= 0 && (int64_t)cr[j] == b;
+      }
+      if (!keep) row[c] = -INFINITY;
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Base-2 log-sum-exp correction of one rank's partial attention output.
+ *
+ * Source: page 3 (sglang dcp kernels.py), _correct_attn_cp_out_kernel and
+ * correct_attn_out.  For every (b, h), with l_n = lses[n][b][h], n < N:
+ *   l_n is replaced by -inf when it is NaN or +inf;
+ *   m = max_n l_n, or 0 when that maximum is -inf;
+ *   final = log2(sum_n 2^(l_n - m)) + m;
+ *   d = lses[rank][b][h] - final (the raw value), replaced by -inf when it
+ *   is NaN or +inf; factor = 2^d;
+ *   vlse[b][h] = final; new_out[h][b][:] = out[b][h][:] * factor.
+ * fp32 inputs, arithmetic in double here; all strides in elements.
+ */
+int oracle_correct_attn_out(const float* out, int64_t B, int64_t H, int64_t D, int64_t o_sb,
+                            int64_t o_sh, int64_t o_sd, const float* lses, int64_t N,
+                            int64_t l_sn, int64_t l_sb, int64_t l_sh, int64_t rank,
+                            double* new_out, int64_t n_sh, int64_t n_sb, int64_t n_sd,
+                            double* vlse, int64_t v_sb, int64_t v_sh) {
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t h = 0; h < H; ++h) {
+      double m = -INFINITY;
+      for (int64_t n = 0; n < N; ++n) {
+        double l = (double)lses[n * l_sn + b * l_sb + h * l_sh];
+        if (isnan(l) || (isinf(l) && l > 0)) l = -INFINITY;
+        if (l > m) m = l;
+      }
+      if (isinf(m) && m < 0) m = 0.0;
+      double acc = 0.0;
+      for (int64_t n = 0; n < N; ++n) {
+        double l = (double)lses[n * l_sn + b * l_sb + h * l_sh];
+        if (isnan(l) || (isinf(l) && l > 0)) l = -INFINITY;
+        acc += exp2(l - m);
+      }
+      double final_lse = log2(acc) + m;
+      double d = (double)lses[rank * l_sn + b * l_sb + h * l_sh] - final_lse;
+      if (isnan(d) || (isinf(d) && d > 0)) d = -INFINITY;
+      double factor = exp2(d);
+      vlse[b * v_sb + h * v_sh] = final_lse;
+      for (int64_t x = 0; x < D; ++x)
+        new_out[h * n_sh + b * n_sb + x * n_sd] = (double)out[b * o_sb + h * o_sh + x * o_sd] * factor;
+    }
+  }
+  return 0;
 }
