@@ -5,7 +5,9 @@
  * Source of the operation: the vLLM-fork page
  * "launcher/dcp2/diffs/02-model_executor_kernels_attention_dsa_candidate_blocks.py.diff"
  * (candidate_blocks.py): _max_with_nan, _block_scores_kernel, _block_scores,
- * select_candidate_blocks / _select_candidate_blocks_impl (non-DCP branch).
+ * select_candidate_blocks / _select_candidate_blocks_impl (non-DCP branch;
+ * the DCP branch's selection after its reduce; the candidate masking after
+ * it), and page 3 (sglang dcp kernels.py) for the log-sum-exp correction.
  *
  * Notation used below.
  *   logits   fp32 [rows, ld_logits] row-major; the first `width` columns of a
@@ -156,6 +158,93 @@ dsa_status_t dsa_select_plan(int64_t rows, int64_t width, int32_t block_size,
 
 /* Static string naming a status code ("DSA_OK", ...); "unknown" otherwise. */
 const char* dsa_status_string(dsa_status_t status);
+
+/*
+ * Selection from a reduced block-score matrix: the part of the page's
+ * decode-context-parallel (DCP) branch of _select_candidate_blocks_impl that
+ * follows its all-reduce.  There each rank scores its share of the columns
+ * (token t on rank t mod W) at the local block size B/W with the pin off
+ * (dsa_block_scores with pin_newest = 0), the element-wise maximum over the
+ * ranks gives the global block scores, and every rank then calls this with
+ * the global bounds so that all ranks pin and select alike.
+ *
+ *   scores      fp32 [rows, ld_scores]: the first nscore columns are block
+ *               scores; nblocks = max(max_global_blocks, 1); columns
+ *               >= min(nscore, nblocks) count as -inf, columns >= nblocks are
+ *               ignored.  May be NULL when nscore == 0.
+ *   global_row_ke  int32 device array, e = global_row_ke[r / row_repeat]:
+ *               the row's global context length.
+ *   pin         block min(floor((e - 1) / global_block_size), nblocks - 1)
+ *               scores +inf; rows with e <= 0 select nothing (all -1).
+ *   out         int32 [rows, ld_out]: the ranking and -1 padding of
+ *               dsa_select_candidate_blocks, k' = min(topk_blocks, nblocks).
+ *
+ * rows == 0 or topk_blocks == 0: DSA_OK, nothing written.
+ * Invalid: negative sizes, row_repeat < 1, global_block_size < 1,
+ *   ld_scores < nscore (nscore > 0), ld_out < topk_blocks, null or
+ *   misaligned pointers when there is work.
+ * Unsupported: nblocks above the LDS limit of dsa_select_candidate_blocks.
+ */
+dsa_status_t dsa_select_from_scores(const float* scores, int64_t rows, int64_t nscore,
+                                    int64_t ld_scores, int64_t max_global_blocks,
+                                    const int32_t* global_row_ke, int32_t row_repeat,
+                                    int32_t global_block_size, int32_t topk_blocks, int32_t* out,
+                                    int64_t ld_out, hipStream_t stream);
+
+/*
+ * Candidate masking of packed logits, in place (page: the masking function
+ * after _select_candidate_blocks_impl, documented as masking packed logits
+ * outside the causal bounds and outside the request-local candidates; its
+ * body is not shown, so this is the plain reading): column c < width of row
+ * r keeps its value when s <= c < e and its request-local block (c - s) / B
+ * is one of candidates[r][0 .. topk_blocks) (negative entries match
+ * nothing); every other column becomes -inf.  Kept columns are not written.
+ * Under DCP pass the local block size: local block b is this rank's share of
+ * global block b, so the candidate ids apply unchanged.
+ *
+ *   candidates  int32 [rows, ld_cand], ld_cand >= topk_blocks (the `out` of
+ *               a selection); may be NULL when topk_blocks == 0.
+ *
+ * rows == 0 or width == 0: DSA_OK, nothing written.
+ * Invalid: negative sizes, block_size < 1, row_repeat < 1, ld_logits <
+ *   width, ld_cand < topk_blocks, null or misaligned pointers when there is
+ *   work.  Rows with 16-byte aligned starts and ld_logits % 4 == 0 are
+ *   written with 16-byte stores.
+ */
+dsa_status_t dsa_mask_candidates(float* logits, int64_t rows, int64_t width, int64_t ld_logits,
+                                 const int32_t* row_ks, const int32_t* row_ke,
+                                 const int32_t* candidates, int64_t ld_cand,
+                                 int32_t topk_blocks, int32_t block_size, int32_t row_repeat,
+                                 hipStream_t stream);
+
+/*
+ * Base-2 log-sum-exp correction of one context-parallel rank's partial
+ * attention output (page 3, sglang dcp kernels.py: _correct_attn_cp_out_kernel
+ * / correct_attn_out).  For every b < B, h < H, with l_n = lses[n][b][h]:
+ *   l_n counts as -inf when it is NaN or +inf; m = max_n l_n (0 if -inf);
+ *   final = log2(sum_n 2^(l_n - m)) + m;
+ *   d = lses[cp_rank][b][h] - final (raw value), -inf if NaN or +inf;
+ *   lse_out[b][h] = final;  new_out[h][b][x] = out[b][h][x] * 2^d, x < D.
+ * All tensors fp32, strides in elements (any sign), caller-owned; fp32
+ * arithmetic (exp2/log2 of the hardware, see the parity tolerance).
+ *
+ *   out      [B, H, D] at out + b*out_sb + h*out_sh + x*out_sd
+ *   lses     [N, B, H] at lses + n*lse_sn + b*lse_sb + h*lse_sh
+ *   new_out  [H, B, D] at new_out + h*new_sh + b*new_sb + x*new_sd
+ *   lse_out  [B, H]    at lse_out + b*lse_out_sb + h*lse_out_sh
+ *
+ * B == 0 or H == 0: DSA_OK, nothing written.
+ * Invalid: negative sizes, N < 1, cp_rank outside [0, N), null or
+ *   misaligned pointers when there is work (out and new_out may be NULL
+ *   when D == 0).  Unit D strides, D % 4 == 0, 16-byte aligned bases and
+ *   B/H strides that are multiples of 4 take 16-byte loads and stores.
+ */
+dsa_status_t dsa_correct_attn_out(const float* out, int64_t B, int64_t H, int64_t D,
+                                  int64_t out_sb, int64_t out_sh, int64_t out_sd,
+                                  const float* lses, int64_t N, int64_t lse_sn, int64_t lse_sb,
+                                  int64_t lse_sh, int64_t cp_rank, float* new_out,
+                                  int64_t new_sh, int64_t new_sb, int64_t new_sd, float* lse_out,
+                                  int64_t lse_out_sb, int64_t lse_out_sh, hipStream_t stream);
 
 #ifdef __cplusplus
 }

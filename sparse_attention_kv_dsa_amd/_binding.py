@@ -56,6 +56,15 @@ def lib() -> ctypes.CDLL:
                 L.dsa_select_plan.restype = ctypes.c_int
                 L.dsa_status_string.argtypes = [ctypes.c_int]
                 L.dsa_status_string.restype = ctypes.c_char_p
+                L.dsa_select_from_scores.argtypes = [vp, i64, i64, i64, i64, vp, i32, i32, i32,
+                                                     vp, i64, vp]
+                L.dsa_select_from_scores.restype = ctypes.c_int
+                L.dsa_mask_candidates.argtypes = [vp, i64, i64, i64, vp, vp, vp, i64, i32, i32,
+                                                  i32, vp]
+                L.dsa_mask_candidates.restype = ctypes.c_int
+                L.dsa_correct_attn_out.argtypes = ([vp] + [i64] * 6 + [vp] + [i64] * 5 + [vp]
+                                                   + [i64] * 3 + [vp, i64, i64, vp])
+                L.dsa_correct_attn_out.restype = ctypes.c_int
                 _lib = L
     return _lib
 
@@ -198,3 +207,79 @@ def select_candidate_blocks(logits: torch.Tensor, row_ks: torch.Tensor | None,
         _ptr(out), _ld(out), _ptr(scores_out), ld_scores, workspace.buf.data_ptr(),
         workspace.buf.numel(), plan, plan_arg, stream)
     _raise(code, "dsa_select_candidate_blocks")
+
+
+def select_from_scores(scores: torch.Tensor, global_row_ke: torch.Tensor, topk_blocks: int,
+                       global_block_size: int, max_global_blocks: int, out: torch.Tensor,
+                       row_repeat: int = 1) -> None:
+    """DCP selection after the reduce (dsa_select_from_scores): ``scores``
+    fp32 [rows, nscore] (the element-wise maximum of every rank's unpinned
+    local block scores), pin from the global ends, -1 padded ids in ``out``."""
+    if scores.dtype != torch.float32 or scores.device.type != "cuda":
+        raise ValueError("scores must be float32 on a HIP device")
+    rows, nscore = scores.shape
+    ld = _ld(scores) if nscore else 1
+    if out.dtype != torch.int32 or out.device != scores.device or out.shape[0] != rows:
+        raise ValueError("out must be int32 [rows, >= topk_blocks] on the scores' device")
+    groups = -(-rows // row_repeat) if row_repeat > 0 else 0
+    ke = _bounds(global_row_ke, "global_row_ke", groups, scores.device)
+    code = lib().dsa_select_from_scores(_ptr(scores) if nscore else None, rows, nscore, ld,
+                                        max_global_blocks, _ptr(ke), row_repeat,
+                                        global_block_size, topk_blocks, _ptr(out), _ld(out),
+                                        _stream(scores.device))
+    _raise(code, "dsa_select_from_scores")
+
+
+def mask_candidates(logits: torch.Tensor, row_ks: torch.Tensor | None, row_ke: torch.Tensor,
+                    candidates: torch.Tensor, topk_blocks: int, block_size: int,
+                    row_repeat: int = 1) -> None:
+    """In place: columns outside [s, e) or outside the row's first
+    ``topk_blocks`` candidate blocks become -inf (dsa_mask_candidates)."""
+    ld = _check_logits(logits)
+    rows, width = logits.shape
+    if candidates.dtype != torch.int32 or candidates.device != logits.device:
+        raise ValueError("candidates must be int32 on the logits' device")
+    if candidates.shape[0] != rows:
+        raise ValueError("candidates must have one row per logits row")
+    groups = -(-rows // row_repeat) if row_repeat > 0 else 0
+    ks = _bounds(row_ks, "row_ks", groups, logits.device)
+    ke = _bounds(row_ke, "row_ke", groups, logits.device)
+    code = lib().dsa_mask_candidates(_ptr(logits), rows, width, ld, _ptr(ks), _ptr(ke),
+                                     _ptr(candidates), _ld(candidates), topk_blocks, block_size,
+                                     row_repeat, _stream(logits.device))
+    _raise(code, "dsa_mask_candidates")
+
+
+def correct_attn_out(out: torch.Tensor, lses: torch.Tensor, cp_rank: int,
+                     new_output: torch.Tensor | None = None,
+                     lse: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Base-2 LSE correction of one rank's partial attention output
+    (dsa_correct_attn_out; page 3, correct_attn_out): fp32 ``out [B, H, D]``
+    (or [B, 1, H, D]) and ``lses [N, B, H]`` (or with a size-1 extra dim) give
+    ``(new_output [H, B, D], lse [B, H])``."""
+    if out.dim() == 4 and out.shape[1] == 1:
+        out = out.squeeze(1)
+    if lses.dim() == 4 and lses.shape[-1] == 1:
+        lses = lses.squeeze(-1)
+    if lses.dim() == 4 and lses.shape[1] == 1:
+        lses = lses.squeeze(1)
+    if out.dim() != 3 or lses.dim() != 3:
+        raise ValueError("expected out [B, H, D] and lses [N, B, H]")
+    for t, name in ((out, "out"), (lses, "lses")):
+        if t.dtype != torch.float32 or t.device.type != "cuda":
+            raise ValueError(f"{name} must be float32 on a HIP device")
+    B, H, D = out.shape
+    N = lses.shape[0]
+    if tuple(lses.shape[1:]) != (B, H):
+        raise ValueError("lses must be [N, B, H] for out [B, H, D]")
+    if new_output is None:
+        new_output = torch.empty((H, B, D), dtype=torch.float32, device=out.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=out.device)
+    if new_output.shape != (H, B, D) or lse.shape != (B, H):
+        raise ValueError("new_output must be [H, B, D] and lse [B, H]")
+    code = lib().dsa_correct_attn_out(
+        _ptr(out), B, H, D, *out.stride(), _ptr(lses), N, *lses.stride(), cp_rank,
+        _ptr(new_output), *new_output.stride(), _ptr(lse), *lse.stride(), _stream(out.device))
+    _raise(code, "dsa_correct_attn_out")
+    return new_output, lse

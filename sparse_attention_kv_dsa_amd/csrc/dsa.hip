@@ -774,6 +774,205 @@ __global__ void __launch_bounds__(kThreads) block_scores_kernel(Params p) {
   }
 }
 
+// Selection from a reduced block-score matrix (the decode-context-parallel
+// branch after its all-reduce): one workgroup per row.  Params reuse:
+// logits = scores [rows, ld] holding `width` columns, ke = global ends,
+// B = global block size, nblocks = max(max_global_blocks, 1).  Columns past
+// min(width, nblocks) are -inf; the pin is floor((e-1)/B) clamped to the
+// last block; rows with e <= 0 select nothing.
+__global__ void __launch_bounds__(1024) select_scores_kernel(Params p) {
+  extern __shared__ uint32_t smem[];
+  const int wave = wave_index();
+  const int nw = blockDim.x >> 6;
+  uint32_t* ctl = smem + p.keys_words;
+  uint32_t* area = ctl + kCtlWords;
+  const int32_t ncopy = p.width < p.nblocks ? (int32_t)p.width : p.nblocks;
+  for (int64_t r = blockIdx.x; r < p.items; r += gridDim.x) {
+    const int64_t e = (int64_t)p.ke[r / p.R];
+    RowGeom g;
+    g.row = p.logits + r * p.ld;
+    g.s = 0;
+    g.lo = 0;
+    g.hi = 0;
+    g.nvb = 0;
+    g.pin = -1;
+    if (e > 0) {
+      const int64_t q = (e - 1) / p.B;  // e - 1 >= 0: truncation is the floor
+      g.nvb = ncopy;
+      g.pin = (int32_t)(q < p.nblocks - 1 ? q : p.nblocks - 1);
+    }
+    g.nsel = g.nvb > g.pin + 1 ? g.nvb : g.pin + 1;
+    select_row_prepare(ctl, area, threadIdx.x, blockDim.x);
+    const int32_t nt = (int32_t)blockDim.x;
+    for (int32_t b0 = 0; b0 < g.nvb; b0 += 4 * nt) {  // four loads in flight per lane
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int32_t b = b0 + j * nt + (int32_t)threadIdx.x;
+        v[j] = g.row[b < g.nvb ? b : g.nvb - 1];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int32_t b = b0 + j * nt + (int32_t)threadIdx.x;
+        if (b < g.nvb) smem[b] = order_key(v[j]);
+      }
+    }
+    __syncthreads();
+    select_row<true>(p, r, g, smem, ctl, area, wave, nw);
+    if (r + gridDim.x < p.items) __syncthreads();  // LDS is reused by the next row
+  }
+}
+
+// ------------------------------------------------------------- masking --
+
+constexpr int kMaskChunk = 8192;                    // columns per work item
+constexpr int kMaskBitWords = kMaskChunk / 32 + 2;  // blocks of one chunk, as bits
+
+struct MaskParams {
+  float* logits;
+  int64_t rows, width, ld;
+  const int32_t* ks;
+  const int32_t* ke;
+  const int32_t* cand;
+  int64_t ld_cand;
+  int32_t k, B, R, b_shift;  // b_shift >= 0: B == 1 << b_shift
+  int32_t vec_ok;            // row starts are 16-byte aligned
+  int64_t nchunks, items;
+};
+
+// Item = r * nchunks + c covers columns [c*kMaskChunk, (c+1)*kMaskChunk) of
+// row r.  A column keeps its value when it lies in [s, e) and its
+// request-local block is one of the row's first k candidates; every other
+// column becomes -inf.  Kept columns are neither read nor written: the
+// kernel only writes.
+__global__ void __launch_bounds__(kThreads) mask_candidates_kernel(MaskParams m) {
+  __shared__ uint32_t bits[kMaskBitWords];
+  const int tid = threadIdx.x;
+  const int nt = blockDim.x;
+  const float ninf = -__builtin_inff();
+  for (int64_t item = blockIdx.x; item < m.items; item += gridDim.x) {
+    const int64_t r = item / m.nchunks;
+    const int64_t c0 = (item - r * m.nchunks) * kMaskChunk;
+    const int64_t c1 = c0 + kMaskChunk < m.width ? c0 + kMaskChunk : m.width;
+    const int64_t grp = r / m.R;
+    const int64_t s = m.ks ? (int64_t)m.ks[grp] : 0;
+    const int64_t e = (int64_t)m.ke[grp];
+    const int64_t lo = c0 > s ? c0 : s;  // in-window columns of this chunk: [lo, hi)
+    const int64_t hi = c1 < e ? c1 : e;
+    int64_t blo = 0, nb = 0;             // their blocks: [blo, blo + nb)
+    if (hi > lo) {
+      blo = (lo - s) / m.B;
+      nb = (hi - 1 - s) / m.B - blo + 1;
+    }
+    for (int w = tid; w < kMaskBitWords; w += nt) bits[w] = 0u;
+    __syncthreads();
+    const int32_t* cr = m.k > 0 ? m.cand + r * m.ld_cand : m.cand;
+    for (int32_t j = tid; j < m.k; j += nt) {
+      const int64_t id = (int64_t)cr[j] - blo;
+      if (cr[j] >= 0 && id >= 0 && id < nb) atomicOr(&bits[id >> 5], 1u << (id & 31));
+    }
+    __syncthreads();
+    float* row = m.logits + r * m.ld;
+    auto kept = [&](int64_t c) -> bool {
+      if (c < lo || c >= hi) return false;
+      const int64_t rel = c - s;
+      const int64_t b = (m.b_shift >= 0 ? (rel >> m.b_shift) : rel / m.B) - blo;
+      return (bits[b >> 5] >> (b & 31)) & 1u;
+    };
+    for (int64_t c = c0 + 4 * (int64_t)tid; c < c1; c += 4 * (int64_t)nt) {
+      const bool k0 = kept(c);
+      const bool k1 = c + 1 < c1 && kept(c + 1);
+      const bool k2 = c + 2 < c1 && kept(c + 2);
+      const bool k3 = c + 3 < c1 && kept(c + 3);
+      if (m.vec_ok && c + 3 < c1 && !(k0 || k1 || k2 || k3)) {
+        *reinterpret_cast<float4*>(row + c) = make_float4(ninf, ninf, ninf, ninf);
+      } else {
+        if (!k0) row[c] = ninf;
+        if (c + 1 < c1 && !k1) row[c + 1] = ninf;
+        if (c + 2 < c1 && !k2) row[c + 2] = ninf;
+        if (c + 3 < c1 && !k3) row[c + 3] = ninf;
+      }
+    }
+    __syncthreads();  // the bitmap is reused by the next item
+  }
+}
+
+// ------------------------------------------------------ LSE correction --
+
+struct LseParams {
+  const float* out;
+  int64_t B, H, D, o_sb, o_sh, o_sd;
+  const float* lses;
+  int64_t N, l_sn, l_sb, l_sh, rank;
+  float* nout;
+  int64_t n_sh, n_sb, n_sd;
+  float* vlse;
+  int64_t v_sb, v_sh;
+  int32_t vec;  // unit D strides, D % 4 == 0, 16-byte aligned rows
+};
+
+__device__ __forceinline__ float wave_fsum(float v) {
+  v += dpp_move<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_move<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_move<0x141>(v);  // row_half_mirror
+  v += dpp_move<0x140>(v);  // row_mirror
+  v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// NaN and +inf count as -inf for the merge.
+__device__ __forceinline__ float lse_clean(float x) {
+  return (x != x || x == __builtin_inff()) ? -__builtin_inff() : x;
+}
+
+// Base-2 log-sum-exp correction of one rank's partial attention output: one
+// wave per (b, h).  Lanes hold the N ranks' LSEs (N > 64 in passes of 64);
+// the wave reduces max and sum, forms final = log2(sum 2^(l - m)) + m and
+// factor = 2^(l_rank - final), then scales the D-vector out[b][h] into
+// new_out[h][b].
+__global__ void __launch_bounds__(kThreads) correct_attn_out_kernel(LseParams q) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = blockDim.x >> 6;
+  const int64_t pairs = q.B * q.H;
+  const float ninf = -__builtin_inff();
+  for (int64_t pr = (int64_t)blockIdx.x * nw + wave_index(); pr < pairs;
+       pr += (int64_t)gridDim.x * nw) {
+    const int64_t b = pr / q.H;
+    const int64_t h = pr - b * q.H;
+    const float* lrow = q.lses + b * q.l_sb + h * q.l_sh;
+    float mx = ninf;
+    for (int64_t n0 = 0; n0 < q.N; n0 += 64) {
+      const int64_t n = n0 + lane;
+      const float l = n < q.N ? lse_clean(lrow[n * q.l_sn]) : ninf;
+      mx = fmaximum(mx, group_max<64>(l));
+    }
+    const float m = mx == ninf ? 0.0f : mx;
+    float acc = 0.0f;
+    for (int64_t n0 = 0; n0 < q.N; n0 += 64) {
+      const int64_t n = n0 + lane;
+      const float l = n < q.N ? lse_clean(lrow[n * q.l_sn]) : ninf;
+      acc += wave_fsum(exp2f(l - m));
+    }
+    const float final_lse = log2f(acc) + m;
+    float d = lrow[q.rank * q.l_sn] - final_lse;
+    d = (d != d || d == __builtin_inff()) ? ninf : d;
+    const float factor = exp2f(d);
+    if (lane == 0) q.vlse[b * q.v_sb + h * q.v_sh] = final_lse;
+    const float* src = q.out + b * q.o_sb + h * q.o_sh;
+    float* dst = q.nout + h * q.n_sh + b * q.n_sb;
+    if (q.vec) {
+      for (int64_t x = 4 * (int64_t)lane; x < q.D; x += 256) {
+        const float4 v = *reinterpret_cast<const float4*>(src + x);
+        *reinterpret_cast<float4*>(dst + x) =
+            make_float4(v.x * factor, v.y * factor, v.z * factor, v.w * factor);
+      }
+    } else {
+      for (int64_t x = lane; x < q.D; x += 64) dst[x * q.n_sd] = src[x * q.o_sd] * factor;
+    }
+  }
+}
+
 __global__ void __launch_bounds__(kThreads) fill_minus_one_kernel(int32_t* out, int64_t rows,
                                                                   int64_t ld, int32_t k) {
   const int64_t n = rows * k;
@@ -1077,4 +1276,130 @@ dsa_status_t dsa_select_candidate_blocks(const float* logits, int64_t rows, int6
                                           0, stream);
 }
 
+dsa_status_t dsa_select_from_scores(const float* scores, int64_t rows, int64_t nscore,
+                                    int64_t ld_scores, int64_t max_global_blocks,
+                                    const int32_t* global_row_ke, int32_t row_repeat,
+                                    int32_t global_block_size, int32_t topk_blocks, int32_t* out,
+                                    int64_t ld_out, hipStream_t stream) {
+  if (rows < 0 || nscore < 0 || max_global_blocks < 0 || row_repeat < 1 ||
+      global_block_size < 1 || topk_blocks < 0)
+    return DSA_ERR_INVALID_ARG;
+  if ((nscore > 0 && ld_scores < nscore) || ld_out < topk_blocks) return DSA_ERR_INVALID_ARG;
+  if (rows == 0 || topk_blocks == 0) return DSA_OK;
+  if (!global_row_ke || !out || misaligned(out, 4)) return DSA_ERR_INVALID_ARG;
+  if (nscore > 0 && (!scores || misaligned(scores, 4))) return DSA_ERR_INVALID_ARG;
+  const int64_t nblocks = max_global_blocks > 1 ? max_global_blocks : 1;
+  if (rows > INT32_MAX || nblocks > INT32_MAX) return DSA_ERR_UNSUPPORTED;
+  const int64_t ww = select_wave_words(nblocks, topk_blocks);
+  if (ww * 4 > (int64_t)kLdsLimit) return DSA_ERR_UNSUPPORTED;
+  Params p = {};
+  p.logits = scores;
+  p.rows = rows;
+  p.width = nscore;
+  p.ld = nscore > 0 ? ld_scores : 1;
+  p.ke = global_row_ke;
+  p.B = global_block_size;
+  p.R = row_repeat;
+  p.pin = 1;
+  p.k = topk_blocks;
+  p.nblocks = (int32_t)nblocks;
+  p.kcap = (int32_t)select_kcap(nblocks, topk_blocks);
+  p.keys_words = (int32_t)select_keys_words(nblocks);
+  p.wave_words = (int32_t)ww;
+  p.out = out;
+  p.ld_out = ld_out;
+  int64_t waves = cdiv(nblocks, 64);
+  if (waves > 16) waves = 16;
+  return launch(reinterpret_cast<void*>(&select_scores_kernel), rows, 64 * (int)waves, 1,
+                (size_t)ww * 4, stream, p);
+}
+
+dsa_status_t dsa_mask_candidates(float* logits, int64_t rows, int64_t width, int64_t ld_logits,
+                                 const int32_t* row_ks, const int32_t* row_ke,
+                                 const int32_t* candidates, int64_t ld_cand,
+                                 int32_t topk_blocks, int32_t block_size, int32_t row_repeat,
+                                 hipStream_t stream) {
+  if (rows < 0 || width < 0 || block_size < 1 || row_repeat < 1 || topk_blocks < 0)
+    return DSA_ERR_INVALID_ARG;
+  if (ld_logits < width || ld_cand < topk_blocks) return DSA_ERR_INVALID_ARG;
+  if (rows == 0 || width == 0) return DSA_OK;
+  if (!logits || !row_ke || misaligned(logits, 4)) return DSA_ERR_INVALID_ARG;
+  if (topk_blocks > 0 && (!candidates || misaligned(candidates, 4))) return DSA_ERR_INVALID_ARG;
+  MaskParams m = {};
+  m.logits = logits;
+  m.rows = rows;
+  m.width = width;
+  m.ld = ld_logits;
+  m.ks = row_ks;
+  m.ke = row_ke;
+  m.cand = candidates;
+  m.ld_cand = ld_cand;
+  m.k = topk_blocks;
+  m.B = block_size;
+  m.R = row_repeat;
+  m.b_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
+  m.vec_ok = !misaligned(logits, 16) && (ld_logits % 4) == 0;
+  m.nchunks = cdiv(width, kMaskChunk);
+  m.items = rows * m.nchunks;
+  int64_t grid = m.items < kMaxGrid ? m.items : kMaxGrid;
+  void* args[] = {&m};
+  hipError_t err = hipLaunchKernel(reinterpret_cast<void*>(&mask_candidates_kernel),
+                                   dim3((unsigned)grid), dim3(kThreads), args, 0, stream);
+  if (err != hipSuccess) {
+    (void)hipGetLastError();
+    return DSA_ERR_HIP;
+  }
+  return DSA_OK;
+}
+
+dsa_status_t dsa_correct_attn_out(const float* out, int64_t B, int64_t H, int64_t D,
+                                  int64_t out_sb, int64_t out_sh, int64_t out_sd,
+                                  const float* lses, int64_t N, int64_t lse_sn, int64_t lse_sb,
+                                  int64_t lse_sh, int64_t cp_rank, float* new_out,
+                                  int64_t new_sh, int64_t new_sb, int64_t new_sd, float* lse_out,
+                                  int64_t lse_out_sb, int64_t lse_out_sh, hipStream_t stream) {
+  if (B < 0 || H < 0 || D < 0 || N < 0) return DSA_ERR_INVALID_ARG;
+  if (B == 0 || H == 0) return DSA_OK;
+  if (N < 1 || cp_rank < 0 || cp_rank >= N) return DSA_ERR_INVALID_ARG;
+  if (!lses || !lse_out || misaligned(lses, 4) || misaligned(lse_out, 4))
+    return DSA_ERR_INVALID_ARG;
+  if (D > 0 && (!out || !new_out || misaligned(out, 4) || misaligned(new_out, 4)))
+    return DSA_ERR_INVALID_ARG;
+  LseParams q = {};
+  q.out = out;
+  q.B = B;
+  q.H = H;
+  q.D = D;
+  q.o_sb = out_sb;
+  q.o_sh = out_sh;
+  q.o_sd = out_sd;
+  q.lses = lses;
+  q.N = N;
+  q.l_sn = lse_sn;
+  q.l_sb = lse_sb;
+  q.l_sh = lse_sh;
+  q.rank = cp_rank;
+  q.nout = new_out;
+  q.n_sh = new_sh;
+  q.n_sb = new_sb;
+  q.n_sd = new_sd;
+  q.vlse = lse_out;
+  q.v_sb = lse_out_sb;
+  q.v_sh = lse_out_sh;
+  q.vec = out_sd == 1 && new_sd == 1 && D % 4 == 0 && !misaligned(out, 16) &&
+          !misaligned(new_out, 16) && out_sb % 4 == 0 && out_sh % 4 == 0 && new_sh % 4 == 0 &&
+          new_sb % 4 == 0;
+  int64_t grid = cdiv(B * H, kWaves);
+  if (grid > 8192) grid = 8192;
+  void* args[] = {&q};
+  hipError_t err = hipLaunchKernel(reinterpret_cast<void*>(&correct_attn_out_kernel),
+                                   dim3((unsigned)grid), dim3(kThreads), args, 0, stream);
+  if (err != hipSuccess) {
+    (void)hipGetLastError();
+    return DSA_ERR_HIP;
+  }
+  return DSA_OK;
+}
+
 }  // extern "C"
+

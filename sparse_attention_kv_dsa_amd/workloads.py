@@ -168,3 +168,76 @@ def sha256(*arrays) -> str:
         if a is not None:
             h.update(np.ascontiguousarray(a).tobytes())
     return h.hexdigest()
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the steps after selection (seeds 100+).  Shapes follow the pages:
+# the decode-context-parallel branch of candidate_blocks.py reduces a
+# [rows, max_global_blocks] score matrix; the LSE correction of page 3 works
+# on out [B, H, D] and lses [N, B, H].  The model dimensions used for the LSE
+# workload (H = 128 heads, D = 512 latent columns, N = 8 ranks) are those of a
+# DeepSeek-style MLA decode with the latent output per head; the pages state
+# no shape for it, so this is the choice made here.
+
+
+@dataclass
+class ScoresWorkload:
+    name: str
+    scores: np.ndarray            # float32 [rows, nscore]: reduced block scores
+    global_row_ke: np.ndarray     # int32 [groups]
+    global_block_size: int
+    max_global_blocks: int
+    topk_blocks: int
+    row_repeat: int
+
+
+def dcp_prefill_scores(rows: int = 8192) -> ScoresWorkload:
+    """DCP share of the large prefill: block scores of 8192 rows over 1024
+    global blocks of 64 tokens, values drawn as the block maxima of the large
+    prefill would fall (uniform(-8, 8) rounded to 1/16: heavy ties), a few
+    NaN and -inf blocks; the global end of query i of either packed request
+    is its context length 28672 + i + 1 (request-local, as the DCP pin
+    reads it), so the pin lands inside the 1024 blocks."""
+    g = _rng(100)
+    x = np.rint(g.uniform(-8.0, 8.0, size=(rows, 1024)).astype(np.float32) * 16.0) / 16.0
+    x = x.astype(np.float32)
+    x[g.random((rows, 1024)) < 1e-4] = np.nan
+    x[g.random((rows, 1024)) < 1e-2] = -np.inf
+    half = rows // 2
+    i = np.arange(rows, dtype=np.int64) % max(half, 1)
+    ends = (28672 + i + 1).astype(np.int32)
+    return ScoresWorkload(f"dcp-prefill-scores-{rows}x1024-g64-k64", x, ends, 64, 1024, 64, 1)
+
+
+def random_scores_case(seed: int, max_rows: int = 40, max_nscore: int = 3000) -> ScoresWorkload:
+    g = _rng(200 + seed)
+    rows = int(g.integers(1, max_rows + 1))
+    R = int(g.integers(1, 4))
+    nscore = int(g.integers(0, max_nscore + 1))
+    mgb = int(g.integers(0, 2 * max(nscore, 1) + 2))
+    G = int(g.integers(1, 200))
+    k = int(g.integers(0, 300))
+    vals = np.array([-2.0, -0.5, 0.25, 1.0, 3.0, np.inf, -np.inf, np.nan], np.float32)
+    x = g.standard_normal((rows, nscore)).astype(np.float32)
+    pick = g.random((rows, nscore)) < 0.3
+    x[pick] = vals[g.integers(0, len(vals), size=int(pick.sum()))]
+    ends = g.integers(-5, mgb * G + 3 * G + 2, size=-(-rows // R)).astype(np.int32)
+    return ScoresWorkload(f"scores-case-{seed}", x, ends, G, mgb, k, R)
+
+
+@dataclass
+class LseWorkload:
+    name: str
+    out: np.ndarray     # float32 [B, H, D]
+    lses: np.ndarray    # float32 [N, B, H] (base-2)
+    cp_rank: int
+
+
+def lse_merge(B: int = 256, H: int = 128, D: int = 512, N: int = 8, seed: int = 300) -> LseWorkload:
+    """Partial MLA attention outputs ~ N(0, 1) and base-2 LSEs ~ 12 + 4 N(0, 1),
+    with 1% of (rank, b, h) entries -inf (a rank that held no context)."""
+    g = _rng(seed)
+    out = g.standard_normal((B, H, D)).astype(np.float32)
+    lses = (12.0 + 4.0 * g.standard_normal((N, B, H))).astype(np.float32)
+    lses[g.random((N, B, H)) < 0.01] = -np.inf
+    return LseWorkload(f"lse-merge-{B}x{H}x{D}-n{N}", out, lses, 3 % N)

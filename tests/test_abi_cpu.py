@@ -137,3 +137,61 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         B.select_candidate_blocks(x, None, torch.zeros(4, dtype=torch.int32), 4, 8,
                                   torch.zeros(4, 4, dtype=torch.int32))
+
+
+# --- the entry points after selection: host-side argument checks (no launch)
+
+def _sfs(**kw):
+    a = dict(scores=FAKE, rows=4, nscore=8, ld=8, mgb=8, ke=FAKE, R=1, G=4, k=4, out=FAKE2, ld_out=4)
+    a.update(kw)
+    return B.lib().dsa_select_from_scores(a["scores"], a["rows"], a["nscore"], a["ld"], a["mgb"],
+                                          a["ke"], a["R"], a["G"], a["k"], a["out"], a["ld_out"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rows=0), 0), (dict(k=0), 0), (dict(rows=0, scores=None, ke=None, out=None), 0),
+    (dict(rows=-1), 1), (dict(nscore=-1), 1), (dict(mgb=-1), 1), (dict(R=0), 1), (dict(G=0), 1),
+    (dict(k=-1), 1), (dict(ld=7), 1), (dict(ld_out=3), 1), (dict(ke=None), 1), (dict(out=None), 1),
+    (dict(out=FAKE2 + 2), 1), (dict(scores=None), 1), (dict(scores=FAKE + 1), 1),
+    (dict(mgb=1 << 20, k=4), 2),                      # the scores do not fit in LDS
+])
+def test_select_from_scores_rejects_on_host(kw, code):
+    assert _sfs(**kw) == code
+
+
+def _mask(**kw):
+    a = dict(logits=FAKE, rows=4, width=64, ld=64, ks=None, ke=FAKE, cand=FAKE2, ld_cand=4, k=4,
+             B=8, R=1)
+    a.update(kw)
+    return B.lib().dsa_mask_candidates(a["logits"], a["rows"], a["width"], a["ld"], a["ks"],
+                                       a["ke"], a["cand"], a["ld_cand"], a["k"], a["B"], a["R"],
+                                       None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rows=0), 0), (dict(width=0), 0), (dict(rows=0, logits=None, ke=None, cand=None), 0),
+    (dict(rows=-1), 1), (dict(width=-1), 1), (dict(B=0), 1), (dict(R=0), 1), (dict(k=-1), 1),
+    (dict(ld=63), 1), (dict(ld_cand=3), 1), (dict(logits=None), 1), (dict(ke=None), 1),
+    (dict(cand=None), 1), (dict(logits=FAKE + 2), 1), (dict(cand=FAKE2 + 1), 1),
+])
+def test_mask_rejects_on_host(kw, code):
+    assert _mask(**kw) == code
+
+
+def _lse(**kw):
+    a = dict(out=FAKE, B=2, H=3, D=8, o=(24, 8, 1), lses=FAKE2, N=4, l=(6, 3, 1), rank=1,
+             new=FAKE, n=(16, 8, 1), v=FAKE2, vs=(3, 1))
+    a.update(kw)
+    return B.lib().dsa_correct_attn_out(a["out"], a["B"], a["H"], a["D"], *a["o"], a["lses"],
+                                        a["N"], *a["l"], a["rank"], a["new"], *a["n"], a["v"],
+                                        *a["vs"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), 0), (dict(H=0), 0), (dict(B=0, out=None, lses=None, new=None, v=None), 0),
+    (dict(B=-1), 1), (dict(D=-1), 1), (dict(N=0), 1), (dict(N=-1), 1), (dict(rank=4), 1),
+    (dict(rank=-1), 1), (dict(lses=None), 1), (dict(v=None), 1), (dict(out=None), 1),
+    (dict(new=None), 1), (dict(lses=FAKE2 + 2), 1), (dict(new=FAKE + 1), 1),
+])
+def test_correct_attn_out_rejects_on_host(kw, code):
+    assert _lse(**kw) == code

@@ -1,0 +1,239 @@
+"""GPU parity for the steps after selection, against the CPU oracle.
+
+- dsa_select_from_scores (the DCP branch after its reduce): ids bit-exact on
+  random cases (NaN, +-inf, ties, clamped pins, ends <= 0, short and
+  truncated score rows, row_repeat) and on the full-size DCP prefill share;
+  plus the DCP decomposition run on the GPU (shards scored by
+  dsa_block_scores with the pin off, reduced with an element-wise maximum)
+  against the unsharded GPU selection.
+- dsa_mask_candidates: bit-exact against the oracle on random cases (odd
+  widths and block sizes, unaligned rows, negative starts) and on the
+  prefill chunk masked with its own selection (sampled rows).
+- dsa_correct_attn_out: within the fp32 tolerance stated below against the
+  oracle's float64 arithmetic, for N up to 70 ranks (more than one pass of
+  64 lanes), strided views, special values and the full-size workload.
+Expected values come only from oracle/.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_kv_dsa_amd as dsa
+from sparse_attention_kv_dsa_amd import workloads
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
+
+
+# ------------------------------------------------------------ select_from_scores
+
+def _gpu_sfs(w, ld_pad=0):
+    rows, nscore = w.scores.shape
+    sc = torch.full((rows, nscore + ld_pad), 12345.0, dtype=torch.float32, device=DEV)
+    sc[:, :nscore] = torch.from_numpy(w.scores).to(DEV)
+    out = torch.full((rows, w.topk_blocks + 2), 777, dtype=torch.int32, device=DEV)
+    dsa.select_from_scores(sc[:, :nscore], _i32(w.global_row_ke), w.topk_blocks,
+                           w.global_block_size, w.max_global_blocks, out[:, :w.topk_blocks],
+                           w.row_repeat)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert (got[:, w.topk_blocks:] == 777).all(), "wrote past topk_blocks"
+    return got[:, :w.topk_blocks]
+
+
+def _oracle_sfs(w):
+    exp = np.empty((w.scores.shape[0], w.topk_blocks), np.int32)
+    oracle.select_from_scores(w.scores, w.global_row_ke, w.topk_blocks, w.global_block_size,
+                              w.max_global_blocks, exp, w.row_repeat)
+    return exp
+
+
+def test_select_from_scores_random_cases():
+    for seed in range(60):
+        w = workloads.random_scores_case(seed)
+        got = _gpu_sfs(w, ld_pad=seed % 3)
+        exp = _oracle_sfs(w)
+        assert np.array_equal(got, exp), (seed, w.scores.shape, w.max_global_blocks, w.topk_blocks)
+
+
+def test_select_from_scores_full_size():
+    w = workloads.dcp_prefill_scores()
+    _say("select_from_scores", w.name)
+    got = _gpu_sfs(w)
+    assert np.array_equal(got, _oracle_sfs(w))
+
+
+@pytest.mark.parametrize("W", [2, 4, 8])
+def test_dcp_decomposition_on_gpu(W):
+    rng = np.random.default_rng(40 + W)
+    rows, width, B, k = 24, 20000, 64, 32
+    x = (rng.standard_normal((rows, width)) + 0.125).astype(np.float32)
+    x[x == 0] = 1.0                                      # no signed zeros in the reduce
+    x[rng.random((rows, width)) < 1e-4] = np.nan
+    ends = rng.integers(0, width + 1, size=rows).astype(np.int32)
+    ends[0] = 0
+    xd = torch.from_numpy(x).to(DEV)
+    nblocks = -(-width // B)
+    reduced = torch.full((rows, nblocks), -float("inf"), dtype=torch.float32, device=DEV)
+    for wr in range(W):
+        local = xd[:, wr::W].contiguous()
+        lend = np.maximum(0, -(-(ends.astype(np.int64) - wr) // W)).astype(np.int32)
+        sc = dsa.block_scores(local, None, _i32(lend), B // W, 1, pin_newest=False)
+        n = min(sc.shape[1], nblocks)
+        reduced[:, :n] = torch.maximum(reduced[:, :n], sc[:, :n])   # NaN propagates
+    got = torch.empty((rows, k), dtype=torch.int32, device=DEV)
+    dsa.select_from_scores(reduced, _i32(ends), k, B, nblocks, got)
+    ref = torch.empty((rows, k), dtype=torch.int32, device=DEV)
+    dsa.select_candidate_blocks(xd, None, _i32(ends), k, B, ref)
+    torch.cuda.synchronize()
+    exp = np.empty((rows, k), np.int32)
+    oracle.select_candidate_blocks(x, None, ends, k, B, exp)
+    assert np.array_equal(got.cpu().numpy(), exp)
+    assert np.array_equal(ref.cpu().numpy(), exp)
+
+
+# ------------------------------------------------------------------- masking
+
+def _dev_rows(x, ld_pad, offset):
+    rows, width = x.shape
+    ld = width + ld_pad
+    flat = torch.full((offset + rows * ld + 4,), 4242.0, dtype=torch.float32, device=DEV)
+    view = flat[offset:offset + rows * ld].view(rows, ld)
+    view[:, :width].copy_(torch.from_numpy(x))
+    return flat, view[:, :width]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_mask_random_cases(seed):
+    rng = np.random.default_rng(500 + seed)
+    for _ in range(6):
+        rows = int(rng.integers(1, 12))
+        R = int(rng.integers(1, 3))
+        width = int(rng.integers(1, 20000))
+        B = int(rng.choice([1, 3, 4, 7, 16, 64, 100, 128]))
+        k = int(rng.integers(0, 40))
+        groups = -(-rows // R)
+        x = rng.standard_normal((rows, width)).astype(np.float32)
+        x[rng.random((rows, width)) < 1e-3] = np.nan
+        starts = None if rng.random() < 0.3 else rng.integers(-5, width, size=groups).astype(np.int32)
+        ends = rng.integers(-3, width + 50, size=groups).astype(np.int32)
+        nb = -(-width // B) + 2
+        cand = rng.integers(-1, nb, size=(rows, max(k, 1) + 1)).astype(np.int32)
+        ld_pad, offset = int(rng.integers(0, 5)), int(rng.integers(0, 4))
+        flat, xd = _dev_rows(x, ld_pad, offset)
+        before = flat.clone()
+        dsa.mask_candidates(xd, None if starts is None else _i32(starts), _i32(ends),
+                            _i32(cand), k, B, R)
+        torch.cuda.synchronize()
+        exp = x.copy()
+        oracle.mask_candidates(exp, starts, ends, cand, k, B, R)
+        got = xd.cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), exp.view(np.uint32)), (seed, rows, width, B, k)
+        # nothing outside the rows' first `width` columns was written
+        changed = (flat != before) & ~(torch.isnan(flat) & torch.isnan(before))
+        mask = torch.zeros_like(changed)
+        mask[offset:offset + rows * (width + ld_pad)].view(rows, width + ld_pad)[:, :width] = True
+        assert not (changed & ~mask).any()
+
+
+def test_mask_prefill_chunk_with_its_selection():
+    w = workloads.config(3)
+    sel = np.empty((w.rows, w.topk_blocks), np.int32)
+    oracle.select_candidate_blocks(w.logits, w.row_ks, w.row_ke, w.topk_blocks, w.block_size,
+                                   sel, w.row_repeat, nthreads=8)
+    xd = torch.from_numpy(w.logits).to(DEV)
+    dsa.mask_candidates(xd, _i32(w.row_ks), _i32(w.row_ke), _i32(sel), w.topk_blocks,
+                        w.block_size, w.row_repeat)
+    torch.cuda.synchronize()
+    rows = np.linspace(0, w.rows - 1, 96).astype(np.int64)
+    exp = np.ascontiguousarray(w.logits[rows])
+    oracle.mask_candidates(exp, w.row_ks[rows], w.row_ke[rows], np.ascontiguousarray(sel[rows]),
+                           w.topk_blocks, w.block_size, 1)
+    got = xd.cpu().numpy()[rows]
+    assert np.array_equal(got.view(np.uint32), exp.view(np.uint32))
+
+
+# ------------------------------------------------------ LSE correction (page 3)
+
+def _lse_tol(ref_new, ref_lse, lses, rank):
+    """fp32 kernel vs float64 oracle.  final = log2(sum 2^(l-m)) + m carries
+    about (N + 4) float ulps of relative error from the exp2 terms, the sum
+    and log2, plus the roundings of l - m and + m (|m|, |final| times 2^-23
+    each); the factor 2^d then has relative error ln2 * |error of d|, with d
+    = local - final adding one more rounding of |d|; the product out *
+    factor adds one ulp.  Bounds below take twice those terms."""
+    N = lses.shape[0]
+    eps = 2.0 ** -23
+    local = lses[rank].astype(np.float64)
+    fin = np.where(np.isfinite(ref_lse), np.abs(ref_lse), 0.0)
+    big = np.maximum(fin, np.where(np.isfinite(local), np.abs(local), 0.0))
+    tol_lse = 2 * ((N + 4) * eps * 1.5 + 2 * eps * fin)
+    tol_d = tol_lse + 2 * eps * (big + fin)
+    rel = np.log(2.0) * tol_d + 2 * eps
+    return tol_lse, rel
+
+
+def _check_lse(out_np, lses_np, rank, new, lse):
+    ref_new, ref_lse = oracle.correct_attn_out(out_np, lses_np, rank)
+    tol_lse, rel = _lse_tol(ref_new, ref_lse, lses_np, rank)
+    lse_np = lse.cpu().numpy().astype(np.float64)
+    same_inf = np.isinf(ref_lse) & (lse_np == ref_lse)
+    assert (same_inf | (np.abs(lse_np - ref_lse) <= tol_lse)).all()
+    new_np = new.cpu().numpy().astype(np.float64)
+    bound = rel.T[:, :, None] * np.abs(ref_new) + 1e-37
+    assert (np.abs(new_np - ref_new) <= bound).all()
+
+
+@pytest.mark.parametrize("N", [1, 2, 8, 64, 70])
+def test_lse_random(N):
+    w = workloads.lse_merge(B=7, H=5, D=36, N=N, seed=310 + N)
+    for rank in sorted({0, N // 2, N - 1}):
+        out = torch.from_numpy(w.out).to(DEV)
+        lses = torch.from_numpy(w.lses).to(DEV)
+        new, lse = dsa.correct_attn_out(out, lses, rank)
+        torch.cuda.synchronize()
+        _check_lse(w.out, w.lses, rank, new, lse)
+
+
+def test_lse_strided_and_special_values():
+    rng = np.random.default_rng(77)
+    B, H, D, N = 6, 4, 64, 5
+    out = rng.standard_normal((B, H, D)).astype(np.float32)
+    lses = (rng.standard_normal((N, B, H)) * 6).astype(np.float32)
+    lses[0, 0, 0] = np.nan
+    lses[1, 0, 1] = np.inf
+    lses[:, 1, 2] = -np.inf
+    lses[2, 2, 3] = np.nan
+    big = torch.zeros((N, B, H, 2), dtype=torch.float32, device=DEV)
+    big[..., 1] = torch.from_numpy(lses).to(DEV)
+    outv = torch.zeros((B, 2, H, D), dtype=torch.float32, device=DEV)
+    outv[:, 0] = torch.from_numpy(out).to(DEV)
+    newv = torch.zeros((H, 2 * B, D + 3), dtype=torch.float32, device=DEV)
+    for rank in range(N):
+        new, lse = dsa.correct_attn_out(outv[:, 0], big[..., 1], rank,
+                                        new_output=newv[:, ::2, 1:D + 1])
+        torch.cuda.synchronize()
+        _check_lse(out, lses, rank, new, lse)
+        assert torch.isfinite(new).all()
+
+
+def test_lse_full_size():
+    w = workloads.lse_merge()
+    _say("lse", w.name)
+    out = torch.from_numpy(w.out).to(DEV)
+    lses = torch.from_numpy(w.lses).to(DEV)
+    new, lse = dsa.correct_attn_out(out, lses, w.cp_rank)
+    torch.cuda.synchronize()
+    bs = np.arange(0, w.out.shape[0], 17)
+    sub_out = np.ascontiguousarray(w.out[bs])
+    sub_l = np.ascontiguousarray(w.lses[:, bs])
+    _check_lse(sub_out, sub_l, w.cp_rank, new[:, bs], lse[bs])
