@@ -60,6 +60,10 @@ def parse():
                     help="short eager run for rocprofv3: no graph, no oracle timing, no context runs")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain copy of this many MiB (counter scale for rocprofv3 --pmc)")
+    ap.add_argument("--op", default="select", choices=["select", "scores", "mask", "lse"],
+                    help="select: candidate-block selection (the headline, default); scores: the "
+                         "DCP selection from reduced scores; mask: candidate masking; lse: the "
+                         "base-2 LSE correction")
     return ap.parse_args()
 
 
@@ -119,12 +123,220 @@ def cpu_baseline(w, budget_s: float):
                       f"in {el:.1f} s, rows split over {threads} threads"}
 
 
+def _time_steps(launch, K, W, copies, dev, use_graph):
+    """W warmup then K timed steps (step i uses input copy i mod copies),
+    captured in a HIP graph unless use_graph is False; returns ms per step."""
+    import torch
+    stream = torch.cuda.current_stream(dev)
+    if use_graph:
+        cap = torch.cuda.Stream(dev)
+        graphs = {}
+        for name, n in (("warm", W), ("timed", K)):
+            g = torch.cuda.CUDAGraph()
+            if n:
+                with torch.cuda.graph(g, stream=cap):
+                    for i in range(n):
+                        launch(i % copies)
+            graphs[name] = g
+        torch.cuda.synchronize()
+        if W:
+            graphs["warm"].replay()
+    else:
+        for i in range(W):
+            launch(i % copies)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    if use_graph:
+        graphs["timed"].replay()
+    else:
+        for i in range(K):
+            launch(i % copies)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / K
+
+
+def bench_next(args):
+    """The rows after selection (one JSON line each): --op scores | mask | lse."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_kv_dsa_amd as dsa
+    from sparse_attention_kv_dsa_amd import workloads
+
+    dev = torch.device("cuda:0")
+    use_graph = not (args.eager or args.profile)
+    K, W = args.steps, args.warmup
+    threads = len(os.sched_getaffinity(0))
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    if args.op == "scores":
+        import oracle
+        w = workloads.dcp_prefill_scores()
+        rows, nscore = w.scores.shape
+        mat = w.scores.nbytes
+        copies = 1 if args.profile else max(1, min(512, int(-(-args.rotate_bytes * 2**30 // mat))))
+        xs = [torch.from_numpy(w.scores).to(dev) for _ in range(copies)]
+        ke = i32(w.global_row_ke)
+        out = torch.empty((rows, w.topk_blocks), dtype=torch.int32, device=dev)
+        dsa.select_from_scores(xs[0], ke, w.topk_blocks, w.global_block_size,
+                               w.max_global_blocks, out)
+        torch.cuda.synchronize()
+        exp = np.empty((rows, w.topk_blocks), np.int32)
+        oracle.select_from_scores(w.scores, w.global_row_ke, w.topk_blocks, w.global_block_size,
+                                  w.max_global_blocks, exp)
+        parity = bool(np.array_equal(out.cpu().numpy(), exp))
+
+        def launch(i):
+            dsa.select_from_scores(xs[i], ke, w.topk_blocks, w.global_block_size,
+                                   w.max_global_blocks, out)
+
+        live = int((w.global_row_ke > 0).sum())
+        read = live * min(nscore, w.max_global_blocks) * 4
+        alg = read + rows * 4 + rows * w.topk_blocks * 4
+        metric = "DCP select-from-scores: score GB/s (fraction of HBM peak), 1 GPU"
+        value_bytes, kernel = read, "select_scores_kernel"
+        cfg = {"workload": w.name, "rows": rows, "nscore": nscore,
+               "max_global_blocks": w.max_global_blocks, "global_block_size": w.global_block_size,
+               "topk_blocks": w.topk_blocks, "input_copies": copies}
+
+        def cpu(budget):
+            sub = max(1, rows // 16)
+            o = np.empty((sub, w.topk_blocks), np.int32)
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                oracle.select_from_scores(np.ascontiguousarray(w.scores[:sub]), w.global_row_ke[:sub],
+                                          w.topk_blocks, w.global_block_size, w.max_global_blocks, o)
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= budget:
+                    break
+            per = el / reps
+            return {"value": round(sub * min(nscore, w.max_global_blocks) * 4 / per / 1e9, 4),
+                    "unit": "GB/s", "cores": 1, "kind": "oracle",
+                    "sample": f"the first {sub} rows of {w.name}, {reps} calls in {el:.1f} s, one thread"}
+    elif args.op == "mask":
+        import oracle
+        w = workloads.config(3)
+        sel = np.empty((w.rows, w.topk_blocks), np.int32)
+        oracle.select_candidate_blocks(w.logits, w.row_ks, w.row_ke, w.topk_blocks, w.block_size,
+                                       sel, w.row_repeat, nthreads=threads)
+        copies = 1 if args.profile else max(1, min(512, int(-(-args.rotate_bytes * 2**30 // w.logits.nbytes))))
+        xs = [torch.from_numpy(w.logits).to(dev) for _ in range(copies)]
+        ks, ke, cd = i32(w.row_ks), i32(w.row_ke), i32(sel)
+        dsa.mask_candidates(xs[0], ks, ke, cd, w.topk_blocks, w.block_size, w.row_repeat)
+        torch.cuda.synchronize()
+        srows = np.linspace(0, w.rows - 1, 64).astype(np.int64)
+        exp = np.ascontiguousarray(w.logits[srows])
+        oracle.mask_candidates(exp, w.row_ks[srows], w.row_ke[srows], np.ascontiguousarray(sel[srows]),
+                               w.topk_blocks, w.block_size, 1)
+        parity = bool(np.array_equal(xs[0].cpu().numpy()[srows].view(np.uint32), exp.view(np.uint32)))
+        # kept columns: in-window columns of selected blocks (neither read nor written)
+        kept = 0
+        for r in range(w.rows):
+            s, e = int(w.row_ks[r]), int(w.row_ke[r])
+            for b in sel[r]:
+                if b >= 0:
+                    lo, hi = max(s + b * w.block_size, s, 0), min(s + (b + 1) * w.block_size, e, w.width)
+                    kept += max(hi - lo, 0)
+        kept = int(kept)
+        written = (w.rows * w.width - kept) * 4
+
+        def launch(i):
+            dsa.mask_candidates(xs[i], ks, ke, cd, w.topk_blocks, w.block_size, w.row_repeat)
+
+        alg = written + w.rows * w.topk_blocks * 4 + w.rows * 8
+        metric = "candidate masking: written GB/s (fraction of HBM peak), 1 GPU"
+        value_bytes, kernel = written, "mask_candidates_kernel"
+        cfg = {"workload": "mask-" + w.name, "rows": w.rows, "width": w.width,
+               "block_size": w.block_size, "topk_blocks": w.topk_blocks, "input_copies": copies,
+               "kept_columns": kept}
+
+        def cpu(budget):
+            sub = 64
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                y = np.ascontiguousarray(w.logits[:sub])
+                oracle.mask_candidates(y, w.row_ks[:sub], w.row_ke[:sub], np.ascontiguousarray(sel[:sub]),
+                                       w.topk_blocks, w.block_size, 1)
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= budget:
+                    break
+            per = el / reps
+            return {"value": round(written * sub / w.rows / per / 1e9, 4), "unit": "GB/s", "cores": 1,
+                    "kind": "oracle",
+                    "sample": f"the first {sub} rows of the prefill chunk, {reps} calls in {el:.1f} s, one thread"}
+    else:
+        import oracle
+        w = workloads.lse_merge()
+        B, H, D = w.out.shape
+        N = w.lses.shape[0]
+        copies = 1 if args.profile else max(1, min(64, int(-(-args.rotate_bytes * 2**30 // w.out.nbytes))))
+        outs = [torch.from_numpy(w.out).to(dev) for _ in range(copies)]
+        lses = torch.from_numpy(w.lses).to(dev)
+        new = torch.empty((H, B, D), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+        dsa.correct_attn_out(outs[0], lses, w.cp_rank, new_output=new, lse=lse)
+        torch.cuda.synchronize()
+        bs = np.arange(0, B, 17)
+        ref_new, ref_lse = oracle.correct_attn_out(np.ascontiguousarray(w.out[bs]),
+                                                   np.ascontiguousarray(w.lses[:, bs]), w.cp_rank)
+        got = new[:, bs].cpu().numpy().astype(np.float64)
+        parity = bool(np.allclose(got, ref_new, rtol=1e-5, atol=0) and
+                      np.allclose(lse[bs].cpu().numpy(), ref_lse, rtol=1e-6, atol=1e-5))
+
+        def launch(i):
+            dsa.correct_attn_out(outs[i], lses, w.cp_rank, new_output=new, lse=lse)
+
+        alg = 2 * B * H * D * 4 + N * B * H * 4 + B * H * 4
+        metric = "DCP LSE correction: HBM GB/s (fraction of HBM peak), 1 GPU"
+        value_bytes, kernel = alg, "correct_attn_out_kernel"
+        cfg = {"workload": w.name, "B": B, "H": H, "D": D, "N": N, "input_copies": copies}
+
+        def cpu(budget):
+            sub = 8
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                oracle.correct_attn_out(np.ascontiguousarray(w.out[:sub]),
+                                        np.ascontiguousarray(w.lses[:, :sub]), w.cp_rank)
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= budget:
+                    break
+            per = el / reps
+            return {"value": round(alg * sub / B / per / 1e9, 4), "unit": "GB/s", "cores": 1,
+                    "kind": "oracle",
+                    "sample": f"{sub} of {B} query rows, {reps} calls in {el:.1f} s, one thread"}
+
+    print(f"# {args.op}: parity vs oracle: {parity}", file=sys.stderr, flush=True)
+    ms = _time_steps(launch, K, W, copies, dev, use_graph)
+    print(f"# timed {K} steps: {ms * 1e3:.2f} us/step", file=sys.stderr, flush=True)
+    alg, value_bytes = int(alg), int(value_bytes)
+    achieved = alg / (ms * 1e-3) / 1e9
+    res = {"metric": metric, "value": round(value_bytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+           "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms, 6),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic", "config": dict(cfg, graph=use_graph), "parity": parity,
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                        "traffic": traffic_for(cfg["workload"], 0),
+                        "algorithmic_bytes_per_launch": alg, "kernel": kernel}}
+    if args.cpu_seconds > 0 and not args.profile:
+        print("# timing the CPU oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu(args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus N > 1 is not supported "
                                    "(rows shard across GPUs with no communication, see DESIGN.md)"}))
         sys.exit(2)
+    if args.op != "select":
+        bench_next(args)
+        return
     import numpy as np
     import torch
 

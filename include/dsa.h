@@ -118,7 +118,7 @@ size_t dsa_select_workspace_bytes(int64_t rows, int64_t width, int32_t block_siz
  *   ld_logits < width, ld_out < topk_blocks, ld_scores < nblocks when
  *   scores_out is given, null logits/row_ke/out when there is work,
  *   misaligned pointers.
- * Unsupported: 4 * (roundup4(nblocks) + 16 + roundup4(max(512, 2*kcap))) > 65536
+ * Unsupported: 4 * (roundup4(nblocks) + 48 + roundup4(max(1024, 2*kcap))) > 65536
  *   with kcap = max(1, min(topk_blocks, nblocks)) (a row's block scores and
  *   select scratch must fit in LDS), or more than 2^31 - 1 rows.
  */

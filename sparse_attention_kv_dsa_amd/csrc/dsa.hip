@@ -302,12 +302,14 @@ struct EmitScore {
 // More than kCandCap candidates (heavy ties at T0, or k in the hundreds)
 // fall back to an exact one-wave radix select over the LDS keys.
 
-constexpr int kCtlWords = 16;   // per-row control words in LDS
-constexpr int kCtlValid = 0;    // #nonzero rank keys (atomic add)
-constexpr int kCtlCand = 1;     // #candidates (atomic add)
-constexpr int kCtlT0 = 2;       // candidate threshold (atomic max)
+constexpr int kCtlWords = 48;       // per-row control words in LDS
+constexpr int kCtlValid = 0;        // #nonzero rank keys
+constexpr int kCtlCand = 1;         // #candidates (atomic add)
+constexpr int kCtlT0 = 2;           // candidate threshold
+constexpr int kCtlSlotCount = 16;   // 16 per-wave slots: nonzero keys
+constexpr int kCtlSlotBound = 32;   // 16 per-wave slots: bound candidates
 constexpr int kCandCap = 256;   // candidates held in LDS (64-bit words)
-constexpr int kAreaMinWords = 2 * kCandCap;
+constexpr int kAreaMinWords = 1024;  // candidates, or one row of 64 maxima per wave
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
@@ -356,30 +358,6 @@ __device__ __forceinline__ uint32_t block_key(const uint32_t* keys, const RowGeo
 // Candidate word: rank key above, inverted id below; 0 for a non-candidate.
 __device__ __forceinline__ uint64_t cand_word(uint32_t rk, uint32_t i) {
   return rk ? (((uint64_t)rk << 32) | (uint64_t)(~i)) : 0ull;
-}
-
-// Bitwise binary search with ballots over N values per lane: the largest T
-// with #(value >= T) >= need (0 if no T >= 1 qualifies).  Once a probe has
-// exactly `need` values at or above it, T is the smallest of those values.
-template <int N>
-__device__ __forceinline__ uint32_t kth_largest_search(const uint32_t* kv, uint32_t need) {
-  uint32_t T = 0u;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = T | (1u << bit);
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int j = 0; j < N; ++j) cnt += (uint32_t)__popcll(__ballot(kv[j] >= cand));
-    if (cnt >= need) {
-      T = cand;
-      if (cnt == need) {
-        uint32_t inv = 0u;  // max of ~v over v >= cand, i.e. ~min
-#pragma unroll
-        for (int j = 0; j < N; ++j) inv = umax(inv, kv[j] >= cand ? ~kv[j] : 0u);
-        return ~(uint32_t)__builtin_amdgcn_readfirstlane((int)group_umax<64>(inv));
-      }
-    }
-  }
-  return T;
 }
 
 // Ranks cand[0, ncand) (distinct words, 0 = empty): slot r < keff of the
@@ -537,66 +515,171 @@ __device__ __forceinline__ void select_row_prepare(uint32_t* ctl, uint32_t* area
   if (tid < kCtlWords) ctl[tid] = 0u;
 }
 
-// The general path of select_row (nsel > 64) with NGM = 64*GPL groups; group
-// of key i = i mod NGM (a group's maximum is an LDS atomic max).
-template <bool WG, int GPL>
+// Candidate bound by radix passes, for larger k: 8-bit digits of the rank
+// keys from the top, one workgroup histogram per pass (LDS atomic adds, which
+// stay cheap under conflicts), wave 0 finds the digit bucket that holds the
+// keff-th largest key; it stops as soon as the keys at or above the bucket's
+// lowest value fit the candidate store (or all 32 bits are fixed).  Leaves
+// T0 in ctl[kCtlT0] and the nonzero count in ctl[kCtlValid].  `hist` is 256
+// zeroed words.
+constexpr int kCtlPrefix = 3;   // radix: digits fixed so far
+constexpr int kCtlRemain = 4;   // radix: keys still needed below the prefix's higher part
+constexpr int kCtlAbove = 5;    // radix: keys above the current bucket
+constexpr int kCtlDone = 6;     // radix: bound final
+
+template <bool WG>
+__device__ __forceinline__ void bound_radix(const RowGeom& g, int32_t k, const uint32_t* keys,
+                                            uint32_t* ctl, uint32_t* hist, int wave, int nw) {
+  const int lane = threadIdx.x & 63;
+  const int nt = nw * 64;
+  const int32_t nsel = g.nsel;
+  uint32_t prefix = 0u, hmask = 0u;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    uint32_t nv = 0u;
+    for (int32_t base = wave * 64; base < nsel; base += nt) {  // wave-uniform
+      const int32_t i = base + lane;
+      const uint32_t rk = select_rank_key(keys, g, i);
+      if (rk != 0u && (rk & hmask) == prefix) atomicAdd(&hist[(rk >> shift) & 255u], 1u);
+      if (shift == 24) nv += (uint32_t)__popcll(__ballot(rk != 0u));
+    }
+    if (shift == 24 && lane == 0 && nv != 0u) atomicAdd(&ctl[kCtlValid], nv);
+    row_barrier<WG>();
+    if (wave == 0) {
+      uint32_t remaining, above;
+      if (shift == 24) {
+        const uint32_t nvalid = ctl[kCtlValid];
+        remaining = (uint32_t)k < nvalid ? (uint32_t)k : nvalid;
+        above = 0u;
+      } else {
+        remaining = ctl[kCtlRemain];
+        above = ctl[kCtlAbove];
+      }
+      // lane l holds bins 255-4l (q = 0) down to 252-4l (q = 3); a0 counts
+      // the matching keys in higher bins (the lanes before this one)
+      uint4* h4 = reinterpret_cast<uint4*>(hist);
+      const uint4 h = h4[63 - lane];
+      h4[63 - lane] = make_uint4(0u, 0u, 0u, 0u);  // zeroed for the next pass
+      const uint32_t tot = h.x + h.y + h.z + h.w;
+      uint32_t inc = tot;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(inc, off);
+        if (lane >= off) inc += y;
+      }
+      const uint32_t a0 = inc - tot, a1 = a0 + h.w, a2 = a1 + h.z, a3 = a2 + h.y;
+      const bool h0 = a0 < remaining && remaining <= a1;
+      const bool h1 = a1 < remaining && remaining <= a2;
+      const bool h2 = a2 < remaining && remaining <= a3;
+      const bool h3 = a3 < remaining && remaining <= a3 + h.x;
+      const uint64_t hit = __ballot(h0 || h1 || h2 || h3);
+      if (lane == 0) {
+        if (hit == 0ull) {  // keff == 0: nothing to select
+          ctl[kCtlT0] = 0xFFFFFFFFu;
+          ctl[kCtlDone] = 1u;
+        }
+      }
+      if (hit != 0ull) {
+        const int src = (int)__builtin_ctzll(hit);
+        const uint32_t qd = h0 ? 0u : (h1 ? 1u : (h2 ? 2u : 3u));
+        const uint32_t aq = h0 ? a0 : (h1 ? a1 : (h2 ? a2 : a3));
+        const uint32_t cq = h0 ? h.w : (h1 ? h.z : (h2 ? h.y : h.x));
+        const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)(255u - 4u * lane - qd), src);
+        const uint32_t above_d = (uint32_t)__builtin_amdgcn_readlane((int)aq, src);
+        const uint32_t cnt_d = (uint32_t)__builtin_amdgcn_readlane((int)cq, src);
+        if (lane == 0) {
+          const uint32_t np = prefix | (d << shift);
+          const uint32_t na = above + above_d;
+          ctl[kCtlPrefix] = np;
+          ctl[kCtlRemain] = remaining - above_d;
+          ctl[kCtlAbove] = na;
+          if (na + cnt_d <= (uint32_t)kCandCap || shift == 0) {
+            ctl[kCtlT0] = np;  // keys >= np: the na above plus the bucket's cnt_d
+            ctl[kCtlDone] = 1u;
+          }
+        }
+      }
+    }
+    row_barrier<WG>();
+    if (ctl[kCtlDone] != 0u) return;  // workgroup-uniform
+    prefix = ctl[kCtlPrefix];
+    hmask |= 255u << shift;
+  }
+}
+
+// Sum over aligned groups of 16 lanes (a DPP row); every lane of the row ends
+// with the row's sum.  All 64 lanes must be active.
+__device__ __forceinline__ uint32_t row_sum16(uint32_t v) {
+  v += dpp_u32<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_u32<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_u32<0x141>(v);  // row_half_mirror
+  v += dpp_u32<0x140>(v);  // row_mirror
+  return v;
+}
+
+// The general path of select_row (nsel > 64).  RADIX: the candidate bound
+// comes from bound_radix; otherwise from 64 group maxima, group l holding
+// the keys i with i mod 64 == l: T0 = the keff-th largest group maximum.
+// Same-address LDS max serialises per lane on this chip, so the maxima and
+// the bound go through per-wave LDS rows and slots, not atomics.
+template <bool WG, bool RADIX>
 __device__ __forceinline__ void select_row_general(const Params& p, const RowGeom& g,
                                                    uint32_t* keys, uint32_t* ctl, uint32_t* area,
                                                    int32_t* out_row, int wave, int nw) {
-  constexpr int NGM = 64 * GPL;
   const int lane = threadIdx.x & 63;
   const int tid = wave * 64 + lane;
   const int nt = nw * 64;
   const int32_t nsel = g.nsel, k = p.k;
-  uint32_t* gm = area;
   uint64_t* cand = reinterpret_cast<uint64_t*>(area);
+  uint32_t t0, nvalid;
 
-  // (A) group maxima and the count of nonzero rank keys.
-  uint32_t nv = 0u;
-  for (int32_t base = wave * 64; base < nsel; base += nt) {  // wave-uniform
-    const int32_t i = base + lane;
-    const uint32_t rk = select_rank_key(keys, g, i);
-    if (rk != 0u) atomicMax(&gm[i & (NGM - 1)], rk);
-    nv += (uint32_t)__popcll(__ballot(rk != 0u));
-  }
-  if (lane == 0 && nv != 0u) atomicAdd(&ctl[kCtlValid], nv);
-  row_barrier<WG>();
-
-  // (C) keff = min(k, #nonzero); T0 = the keff-th largest group maximum.
-  // Wave w tests a slice of the maxima: v qualifies when #(maxima >= v) >=
-  // keff (one ballot per slot); the largest qualifying v goes to ctl[kCtlT0].
-  const uint32_t nvalid = ctl[kCtlValid];
-  const int32_t keff = (uint32_t)k < nvalid ? k : (int32_t)nvalid;
-  {
-    uint32_t gv[GPL];
-#pragma unroll
-    for (int s = 0; s < GPL; ++s) gv[s] = gm[s * 64 + lane];
-    const int32_t len = (NGM + nw - 1) / nw;
+  if constexpr (RADIX) {
+    bound_radix<WG>(g, k, keys, ctl, area, wave, nw);
+    t0 = ctl[kCtlT0];
+    nvalid = ctl[kCtlValid];
+  } else {
+    // (A) per lane: maximum of its keys (all in group `lane`), into this
+    // wave's row of `area`; per wave: its count of nonzero keys.
+    uint32_t tmax = 0u, nv = 0u;
+    for (int32_t base = wave * 64; base < nsel; base += nt) {  // wave-uniform
+      const uint32_t rk = select_rank_key(keys, g, base + lane);
+      tmax = umax(tmax, rk);
+      nv += (uint32_t)__popcll(__ballot(rk != 0u));
+    }
+    area[wave * 64 + lane] = tmax;
+    if (lane == 0) ctl[kCtlSlotCount + wave] = nv;
+    row_barrier<WG>();
+    // (C) every wave: the 64 group maxima (maximum over the waves' rows) and
+    // keff; then a slice of the maxima tested against all of them: v
+    // qualifies when #(maxima >= v) >= keff.  The wave's largest qualifying
+    // v goes to its slot.
+    uint32_t gmx = 0u;
+    for (int w = 0; w < nw; ++w) gmx = umax(gmx, area[w * 64 + lane]);
+    nvalid = (uint32_t)__builtin_amdgcn_readlane(
+        (int)row_sum16(lane < nw ? ctl[kCtlSlotCount + lane] : 0u), 0);
+    const uint32_t kq = (uint32_t)k < nvalid ? (uint32_t)k : nvalid;
+    const int32_t len = (64 + nw - 1) / nw;
     const int32_t l0 = wave * len;
-    const int32_t l1 = l0 + len < NGM ? l0 + len : NGM;
+    const int32_t l1 = l0 + len < 64 ? l0 + len : 64;
     uint32_t best = 0u;
     for (int32_t l = l0; l < l1; ++l) {  // wave-uniform
-      uint32_t src = gv[0];
-#pragma unroll
-      for (int s = 1; s < GPL; ++s) src = (l >> 6) == s ? gv[s] : src;
-      const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)src, l & 63);
-      uint32_t c = 0u;
-#pragma unroll
-      for (int s = 0; s < GPL; ++s) c += (uint32_t)__popcll(__ballot(gv[s] >= v));
-      best = (c >= (uint32_t)keff && v > best) ? v : best;
+      const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)gmx, l);
+      const uint32_t c = (uint32_t)__popcll(__ballot(gmx >= v));
+      best = (c >= kq && v > best) ? v : best;
     }
-    if (lane == 0 && best != 0u) atomicMax(&ctl[kCtlT0], best);
+    if (lane == 0) ctl[kCtlSlotBound + wave] = best;
+    row_barrier<WG>();
+    t0 = (uint32_t)__builtin_amdgcn_readlane(
+        (int)group_umax<16>(lane < nw ? ctl[kCtlSlotBound + lane] : 0u), 0);
   }
-  row_barrier<WG>();
+  const int32_t keff = (uint32_t)k < nvalid ? k : (int32_t)nvalid;
 
   // (E) compact the candidates (keys >= T0) into LDS.
   {
-    const uint32_t t0r = ctl[kCtlT0];
-    const uint32_t t0 = t0r > 1u ? t0r : 1u;
+    const uint32_t tt = t0 > 1u ? t0 : 1u;
     for (int32_t base = wave * 64; base < nsel; base += nt) {  // wave-uniform
       const int32_t i = base + lane;
       const uint32_t rk = select_rank_key(keys, g, i);
-      const bool c = rk >= t0;
+      const bool c = rk >= tt;
       const uint64_t m = __ballot(c);
       if (m != 0ull) {
         uint32_t b0 = 0u;
@@ -659,9 +742,8 @@ __device__ __forceinline__ void select_row(const Params& p, int64_t r, const Row
     }
     return;
   }
-  if (k <= 32) select_row_general<WG, 1>(p, g, keys, ctl, area, out_row, wave, nw);
-  else if (k <= 64) select_row_general<WG, 2>(p, g, keys, ctl, area, out_row, wave, nw);
-  else select_row_general<WG, 4>(p, g, keys, ctl, area, out_row, wave, nw);
+  if (k <= 32) select_row_general<WG, false>(p, g, keys, ctl, area, out_row, wave, nw);
+  else select_row_general<WG, true>(p, g, keys, ctl, area, out_row, wave, nw);
 }
 
 // Plan "wave": one wave per row, blockDim/64 rows per workgroup, no barrier.
@@ -1308,8 +1390,11 @@ dsa_status_t dsa_select_from_scores(const float* scores, int64_t rows, int64_t n
   p.wave_words = (int32_t)ww;
   p.out = out;
   p.ld_out = ld_out;
+  // Few rows: a wide workgroup per row (latency); many rows: four waves per
+  // row, so that several rows' selects share each CU (throughput).
   int64_t waves = cdiv(nblocks, 64);
   if (waves > 16) waves = 16;
+  if (rows >= 1024 && waves > kWaves) waves = kWaves;
   return launch(reinterpret_cast<void*>(&select_scores_kernel), rows, 64 * (int)waves, 1,
                 (size_t)ww * 4, stream, p);
 }

@@ -92,8 +92,8 @@ def _sel(**kw):
     (dict(ws=None, plan=2), 3), (dict(ws_bytes=100, plan=2), 3), (dict(ws=FAKE + 2, plan=2), 3),
     (dict(ws=None, plan=2, cb=3), 3),
     (dict(width=1 << 20, ld=1 << 20, B=16, k=4096, ld_out=4096), 2),  # keys do not fit in LDS
-    (dict(width=15856 * 4 + 4, ld=1 << 16, B=4, k=3, ld_out=3), 2),   # 15860 + 16 + 512 words > 16384
-    (dict(width=15856 * 4, ld=1 << 16, B=4, k=3, ld_out=3, plan=2, ws=None), 3),  # 15856 + 16 + 512 fits
+    (dict(width=15312 * 4 + 4, ld=1 << 16, B=4, k=3, ld_out=3), 2),   # 15316 + 48 + 1024 words > 16384
+    (dict(width=15312 * 4, ld=1 << 16, B=4, k=3, ld_out=3, plan=2, ws=None), 3),  # 15312 + 48 + 1024 fits
     (dict(rows=0), 0), (dict(k=0), 0), (dict(rows=0, logits=None, ke=None, out=None), 0),
 ])
 def test_select_rejects_on_host(kw, code):
