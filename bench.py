@@ -123,6 +123,26 @@ def cpu_baseline(w, budget_s: float):
                       f"in {el:.1f} s, rows split over {threads} threads"}
 
 
+def _calib_copy(args, dev):
+    """One plain device copy of --calib-copy-mib MiB: its hardware read/write
+    byte counters give the scale for the kernels' counters."""
+    if not args.calib_copy_mib:
+        return
+    import torch
+    from sparse_attention_kv_dsa_amd import build as dsa_build
+    vp = ctypes.c_void_p
+    calib = ctypes.CDLL(dsa_build.lib_path("libdsa_calib.so"))
+    calib.dsa_calib_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
+    nbytes = args.calib_copy_mib << 20
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    assert calib.dsa_calib_copy(a.data_ptr(), b.data_ptr(), nbytes,
+                                vp(torch.cuda.current_stream(dev).cuda_stream)) == 0
+    torch.cuda.synchronize()
+    print(f"# calibration copy of {args.calib_copy_mib} MiB done", file=sys.stderr, flush=True)
+
+
 def _time_steps(launch, K, W, copies, dev, use_graph):
     """W warmup then K timed steps (step i uses input copy i mod copies),
     captured in a HIP graph unless use_graph is False; returns ms per step."""
@@ -310,6 +330,7 @@ def bench_next(args):
                     "sample": f"{sub} of {B} query rows, {reps} calls in {el:.1f} s, one thread"}
 
     print(f"# {args.op}: parity vs oracle: {parity}", file=sys.stderr, flush=True)
+    _calib_copy(args, dev)
     ms = _time_steps(launch, K, W, copies, dev, use_graph)
     print(f"# timed {K} steps: {ms * 1e3:.2f} us/step", file=sys.stderr, flush=True)
     alg, value_bytes = int(alg), int(value_bytes)
@@ -401,17 +422,7 @@ def main():
         if code:
             raise RuntimeError(f"dsa_select_candidate_blocks: {dsa.status_string(code)}")
 
-    if args.calib_copy_mib:
-        calib = ctypes.CDLL(dsa_build.lib_path("libdsa_calib.so"))
-        calib.dsa_calib_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
-        nbytes = args.calib_copy_mib << 20
-        a = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        assert calib.dsa_calib_copy(a.data_ptr(), b.data_ptr(), nbytes,
-                                    vp(torch.cuda.current_stream(dev).cuda_stream)) == 0
-        torch.cuda.synchronize()
-        print(f"# calibration copy of {args.calib_copy_mib} MiB done", file=sys.stderr, flush=True)
+    _calib_copy(args, dev)
 
     stream = torch.cuda.current_stream(dev)
     use_graph = not (args.eager or args.profile)
