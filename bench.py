@@ -143,6 +143,59 @@ def _calib_copy(args, dev):
     print(f"# calibration copy of {args.calib_copy_mib} MiB done", file=sys.stderr, flush=True)
 
 
+def _stream_context(dev, achieved, kind):
+    """This GPU's own ceilings beside a result: the launch floor of an empty
+    kernel replayed from a graph, and plain 2 GiB read, fill (write-only) and
+    copy streams (libdsa_calib.so).  `achieved` (GB/s) is also given as a
+    fraction of the `kind` stream that matches the kernel's traffic."""
+    import torch
+    from sparse_attention_kv_dsa_amd import build as dsa_build
+    vp = ctypes.c_void_p
+    calib = ctypes.CDLL(dsa_build.lib_path("libdsa_calib.so"))
+    calib.dsa_calib_empty.argtypes = [vp]
+    calib.dsa_calib_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
+    calib.dsa_calib_fill.argtypes = [vp, ctypes.c_size_t, ctypes.c_uint32, vp]
+    calib.dsa_calib_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
+    stream = torch.cuda.current_stream(dev)
+    sp = vp(stream.cuda_stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream(dev)):
+        for _ in range(1000):
+            calib.dsa_calib_empty(vp(torch.cuda.current_stream(dev).cuda_stream))
+    g.replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    floor_us = e0.elapsed_time(e1)          # 1000 launches -> ms == us per launch
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty(calib.dsa_calib_read_sink_words(), dtype=torch.int32, device=dev)
+    half = nbytes // 2
+    calls = {
+        "read": (lambda: calib.dsa_calib_read(buf.data_ptr(), nbytes, sink.data_ptr(), sp), nbytes),
+        "fill": (lambda: calib.dsa_calib_fill(buf.data_ptr(), nbytes, 0xFF800000, sp), nbytes),
+        "copy": (lambda: calib.dsa_calib_copy(buf.data_ptr(), buf.data_ptr() + half, half, sp),
+                 2 * half),
+    }
+    ctx = {"graph_launch_floor_us": round(floor_us, 3)}
+    for name, (call, moved) in calls.items():
+        for _ in range(2):
+            assert call() == 0
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(5):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ctx[f"{name}_stream_GBps"] = round(5 * moved / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del buf
+    ctx[f"frac_of_{kind}_stream"] = round(achieved / ctx[f"{kind}_stream_GBps"], 4)
+    return ctx
+
+
 def _time_steps(launch, K, W, copies, dev, use_graph):
     """W warmup then K timed steps (step i uses input copy i mod copies),
     captured in a HIP graph unless use_graph is False; returns ms per step."""
@@ -343,6 +396,9 @@ def bench_next(args):
                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                         "traffic": traffic_for(cfg["workload"], 0),
                         "algorithmic_bytes_per_launch": alg, "kernel": kernel}}
+    if not args.profile:
+        res["context"] = _stream_context(dev, achieved, {"scores": "read", "mask": "fill",
+                                                          "lse": "copy"}[args.op])
     if args.cpu_seconds > 0 and not args.profile:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu(args.cpu_seconds)
@@ -486,38 +542,7 @@ def main():
     }
 
     if not args.profile:
-        # context: launch floor and a plain read stream on this GPU
-        calib = ctypes.CDLL(dsa_build.lib_path("libdsa_calib.so"))
-        calib.dsa_calib_empty.argtypes = [vp]
-        calib.dsa_calib_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=torch.cuda.Stream(dev)):
-            for _ in range(1000):
-                calib.dsa_calib_empty(vp(torch.cuda.current_stream(dev).cuda_stream))
-        g.replay()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        floor_us = e0.elapsed_time(e1)          # 1000 launches -> ms == us per launch
-        nbytes = 2 << 30
-        buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
-        sink = torch.empty(calib.dsa_calib_read_sink_words(), dtype=torch.int32, device=dev)
-        sp = vp(stream.cuda_stream)
-        for _ in range(2):
-            calib.dsa_calib_read(buf.data_ptr(), nbytes, sink.data_ptr(), sp)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(5):
-            calib.dsa_calib_read(buf.data_ptr(), nbytes, sink.data_ptr(), sp)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        read_gbps = 5 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
-        del buf
-        res["context"] = {"graph_launch_floor_us": round(floor_us, 3),
-                          "read_stream_GBps": round(read_gbps, 1),
-                          "frac_of_read_stream": round(achieved / read_gbps, 4)}
+        res["context"] = _stream_context(dev, achieved, "read")
         if args.cpu_seconds > 0:
             print("# timing the CPU oracle", file=sys.stderr, flush=True)
             res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

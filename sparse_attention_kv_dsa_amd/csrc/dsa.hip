@@ -926,7 +926,9 @@ struct MaskParams {
 // row r.  A column keeps its value when it lies in [s, e) and its
 // request-local block is one of the row's first k candidates; every other
 // column becomes -inf.  Kept columns are neither read nor written: the
-// kernel only writes.
+// kernel only writes.  The candidate ids load beside the bounds (one memory
+// round trip before the first store), and a chunk with no in-window column
+// builds no bitmap.
 __global__ void __launch_bounds__(kThreads) mask_candidates_kernel(MaskParams m) {
   __shared__ uint32_t bits[kMaskBitWords];
   const int tid = threadIdx.x;
@@ -937,45 +939,73 @@ __global__ void __launch_bounds__(kThreads) mask_candidates_kernel(MaskParams m)
     const int64_t c0 = (item - r * m.nchunks) * kMaskChunk;
     const int64_t c1 = c0 + kMaskChunk < m.width ? c0 + kMaskChunk : m.width;
     const int64_t grp = r / m.R;
+    const int32_t* cr = m.k > 0 ? m.cand + r * m.ld_cand : m.cand;
+    const int32_t cid = tid < m.k ? cr[tid] : -1;  // issued before the bounds are known
     const int64_t s = m.ks ? (int64_t)m.ks[grp] : 0;
     const int64_t e = (int64_t)m.ke[grp];
     const int64_t lo = c0 > s ? c0 : s;  // in-window columns of this chunk: [lo, hi)
     const int64_t hi = c1 < e ? c1 : e;
     int64_t blo = 0, nb = 0;             // their blocks: [blo, blo + nb)
-    if (hi > lo) {
+    if (hi > lo) {  // workgroup-uniform
       blo = (lo - s) / m.B;
       nb = (hi - 1 - s) / m.B - blo + 1;
+      const int32_t nw = (int32_t)((nb + 31) >> 5);
+      for (int w = tid; w < nw; w += nt) bits[w] = 0u;
+      __syncthreads();
+      for (int32_t j = tid; j < m.k; j += nt) {
+        const int32_t cj = j == tid ? cid : cr[j];
+        const int64_t id = (int64_t)cj - blo;
+        if (cj >= 0 && id >= 0 && id < nb) atomicOr(&bits[id >> 5], 1u << (id & 31));
+      }
+      __syncthreads();
     }
-    for (int w = tid; w < kMaskBitWords; w += nt) bits[w] = 0u;
-    __syncthreads();
-    const int32_t* cr = m.k > 0 ? m.cand + r * m.ld_cand : m.cand;
-    for (int32_t j = tid; j < m.k; j += nt) {
-      const int64_t id = (int64_t)cr[j] - blo;
-      if (cr[j] >= 0 && id >= 0 && id < nb) atomicOr(&bits[id >> 5], 1u << (id & 31));
-    }
-    __syncthreads();
     float* row = m.logits + r * m.ld;
+    // Columns [a, b) all become -inf: 16-byte stores where the row allows.
+    auto fill = [&](int64_t a, int64_t b) {
+      if (!m.vec_ok) {
+        for (int64_t c = a + tid; c < b; c += nt) row[c] = ninf;
+        return;
+      }
+      int64_t a4 = (a + 3) & ~(int64_t)3;  // [a4, b4): whole aligned float4s
+      int64_t b4 = b & ~(int64_t)3;
+      if (b4 < a4) a4 = b4 = a;            // fewer than one: all scalar (tail)
+      for (int64_t c = a4 + 4 * (int64_t)tid; c < b4; c += 4 * (int64_t)nt)
+        *reinterpret_cast<float4*>(row + c) = make_float4(ninf, ninf, ninf, ninf);
+      if (tid < a4 - a) row[a + tid] = ninf;   // at most 3 columns before
+      if (tid < b - b4) row[b4 + tid] = ninf;  // at most 3 after (all, when short)
+    };
+    const int64_t wlo = hi > lo ? lo : c1;  // an empty window leaves nothing to test
+    const int64_t whi = hi > lo ? hi : c1;
+    fill(c0, wlo);
+    fill(whi, c1);
+    // In-window columns: -inf unless the column's block is a candidate.
     auto kept = [&](int64_t c) -> bool {
-      if (c < lo || c >= hi) return false;
       const int64_t rel = c - s;
       const int64_t b = (m.b_shift >= 0 ? (rel >> m.b_shift) : rel / m.B) - blo;
       return (bits[b >> 5] >> (b & 31)) & 1u;
     };
-    for (int64_t c = c0 + 4 * (int64_t)tid; c < c1; c += 4 * (int64_t)nt) {
-      const bool k0 = kept(c);
-      const bool k1 = c + 1 < c1 && kept(c + 1);
-      const bool k2 = c + 2 < c1 && kept(c + 2);
-      const bool k3 = c + 3 < c1 && kept(c + 3);
-      if (m.vec_ok && c + 3 < c1 && !(k0 || k1 || k2 || k3)) {
-        *reinterpret_cast<float4*>(row + c) = make_float4(ninf, ninf, ninf, ninf);
-      } else {
-        if (!k0) row[c] = ninf;
-        if (c + 1 < c1 && !k1) row[c + 1] = ninf;
-        if (c + 2 < c1 && !k2) row[c + 2] = ninf;
-        if (c + 3 < c1 && !k3) row[c + 3] = ninf;
+    if (m.vec_ok) {
+      int64_t a4 = (wlo + 3) & ~(int64_t)3;
+      int64_t b4 = whi & ~(int64_t)3;
+      if (b4 < a4) a4 = b4 = wlo;
+      for (int64_t c = a4 + 4 * (int64_t)tid; c < b4; c += 4 * (int64_t)nt) {
+        const bool k0 = kept(c), k1 = kept(c + 1), k2 = kept(c + 2), k3 = kept(c + 3);
+        if (!(k0 || k1 || k2 || k3)) {
+          *reinterpret_cast<float4*>(row + c) = make_float4(ninf, ninf, ninf, ninf);
+        } else {
+          if (!k0) row[c] = ninf;
+          if (!k1) row[c + 1] = ninf;
+          if (!k2) row[c + 2] = ninf;
+          if (!k3) row[c + 3] = ninf;
+        }
       }
+      if (tid < a4 - wlo && !kept(wlo + tid)) row[wlo + tid] = ninf;
+      if (tid < whi - b4 && !kept(b4 + tid)) row[b4 + tid] = ninf;
+    } else {
+      for (int64_t c = wlo + tid; c < whi; c += nt)
+        if (!kept(c)) row[c] = ninf;
     }
-    __syncthreads();  // the bitmap is reused by the next item
+    if (hi > lo) __syncthreads();  // the bitmap is reused by the next item
   }
 }
 

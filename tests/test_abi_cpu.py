@@ -129,6 +129,11 @@ def test_calib_rejects_on_host():
     assert L.dsa_calib_copy(FAKE, FAKE2, 0, None) == 0
     assert L.dsa_calib_read(FAKE, 16, None, None) == 1
     assert L.dsa_calib_read_sink_words() >= 1
+    L.dsa_calib_fill.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p]
+    assert L.dsa_calib_fill(FAKE + 8, 16, 0, None) == 1
+    assert L.dsa_calib_fill(FAKE, 24, 0, None) == 1
+    assert L.dsa_calib_fill(None, 16, 0, None) == 1
+    assert L.dsa_calib_fill(FAKE, 0, 0, None) == 0
 
 
 def test_binding_refuses_cpu_tensors():
