@@ -177,13 +177,17 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 // Streams blocks [b0, b1) (b1 <= nvb) of a row on the vector path: s >= 0,
 // (row + s) 16-byte aligned and width % 4 == 0, so every float4 that holds an
 // in-window column lies inside the row.  B = 4*G.  The chunk's 1 KiB tiles
-// are dealt to `nw` waves; this is wave `wv`.  Calls emit(b, max) once per
-// block, from one lane of the block.
+// are dealt to `nw` waves; this is wave `wv`, which takes tiles wv, wv + nw,
+// ... in rounds of U.  Calls emit(b, max) once per block, from one lane of
+// the block.
 //
 // The loads are branch-free: a lane past the chunk's last unit re-reads that
-// unit (same cache line) and masks it, so all U loads of a lane issue back to
-// back.
-template <int G, int U, class Emit>
+// unit (same cache line) and masks it.  ROLL (for emits into LDS): tile j's
+// load for the next round is issued as soon as tile j has been reduced, so U
+// loads stay in flight across rounds instead of draining at each round's end
+// (emits into HBM would count against the same in-order load counter, so
+// those callers take whole rounds).
+template <int G, int U, bool ROLL, class Emit>
 __device__ __forceinline__ void stream_vec(const RowGeom& g, int32_t b0, int32_t b1, int wv,
                                            int nw, const Emit& emit) {
   const int lane = threadIdx.x & 63;
@@ -195,30 +199,49 @@ __device__ __forceinline__ void stream_vec(const RowGeom& g, int32_t b0, int32_t
   const int32_t ntiles = (ue - ub + 63) >> 6;
   const float ninf = -__builtin_inff();
   const char* cbase = reinterpret_cast<const char*>(base);
-  for (int32_t t0 = wv; t0 < ntiles; t0 += nw * U) {
-    float4 v[U];
+  // uniform base + 32-bit byte offset: the scalar-base form of the load
+  auto load = [&](int32_t t) -> float4 {
+    const int32_t u = ub + (t << 6) + lane;
+    const uint32_t off = (uint32_t)(u < ue ? u : ue - 1) << 4;
+    return *reinterpret_cast<const float4*>(cbase + off);
+  };
+  auto reduce = [&](int32_t t, const float4& x4) {
+    const int32_t u = ub + (t << 6) + lane;
+    const int32_t lim = u < ue ? span - 4 * u : 0;  // valid columns in this unit
+    const float x = lim > 0 ? x4.x : ninf;
+    const float y = lim > 1 ? x4.y : ninf;
+    const float z = lim > 2 ? x4.z : ninf;
+    const float w = lim > 3 ? x4.w : ninf;
+    float m = fmaximum(fmaximum(x, y), fmaximum(z, w));
+    m = group_max<G>(m);
+    if (t < ntiles) {
+      const int32_t b = b0 + (((t << 6) + lane) / G);
+      if ((lane % G) == 0 && b < b1) emit(b, m);
+    }
+  };
+  if (wv >= ntiles) return;
+  const int32_t step = nw * U;
+  float4 v[U];
+  if constexpr (ROLL) {
+    const int32_t rounds = (ntiles - wv + step - 1) / step;  // wave-uniform, >= 1
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-      // uniform base + 32-bit byte offset: the scalar-base form of the load
-      const int32_t u = ub + ((t0 + j * nw) << 6) + lane;
-      const uint32_t off = (uint32_t)(u < ue ? u : ue - 1) << 4;
-      v[j] = *reinterpret_cast<const float4*>(cbase + off);
+    for (int j = 0; j < U; ++j) v[j] = load(wv + j * nw);
+    int32_t t0 = wv;
+    for (int32_t r = 1; r < rounds; ++r, t0 += step) {
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        reduce(t0 + j * nw, v[j]);
+        v[j] = load(t0 + step + j * nw);
+      }
     }
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const int32_t t = t0 + j * nw;
-      const int32_t u = ub + (t << 6) + lane;
-      const int32_t lim = u < ue ? span - 4 * u : 0;  // valid columns in this unit
-      const float x = lim > 0 ? v[j].x : ninf;
-      const float y = lim > 1 ? v[j].y : ninf;
-      const float z = lim > 2 ? v[j].z : ninf;
-      const float w = lim > 3 ? v[j].w : ninf;
-      float m = fmaximum(fmaximum(x, y), fmaximum(z, w));
-      m = group_max<G>(m);
-      if (t < ntiles) {
-        const int32_t b = b0 + (((t << 6) + lane) / G);
-        if ((lane % G) == 0 && b < b1) emit(b, m);
-      }
+    for (int j = 0; j < U; ++j) reduce(t0 + j * nw, v[j]);
+  } else {
+    for (int32_t t0 = wv; t0 < ntiles; t0 += step) {
+#pragma unroll
+      for (int j = 0; j < U; ++j) v[j] = load(t0 + j * nw);
+#pragma unroll
+      for (int j = 0; j < U; ++j) reduce(t0 + j * nw, v[j]);
     }
   }
 }
@@ -258,13 +281,13 @@ __device__ __forceinline__ void stream_scalar(const RowGeom& g, int32_t B, int32
   }
 }
 
-template <int G, int U, class Emit>
+template <int G, int U, bool ROLL, class Emit>
 __device__ __forceinline__ void stream_blocks(const Params& p, const RowGeom& g, int32_t b0,
                                               int32_t b1, int wv, int nw, const Emit& emit) {
   if (b1 <= b0) return;
   if constexpr (G > 0) {
     if (p.vec_ok && g.s >= 0 && ((reinterpret_cast<uintptr_t>(g.row + g.s) & 15u) == 0)) {
-      stream_vec<G, U>(g, b0, b1, wv, nw, emit);
+      stream_vec<G, U, ROLL>(g, b0, b1, wv, nw, emit);
       return;
     }
   }
@@ -759,7 +782,7 @@ __global__ void __launch_bounds__(kThreads) select_wave_rows_kernel(Params p) {
   for (int64_t r = (int64_t)blockIdx.x * nw + wave; r < p.items; r += (int64_t)gridDim.x * nw) {
     const RowGeom g = row_geom(p, r, true);
     select_row_prepare(ctl, area, threadIdx.x & 63, 64);
-    stream_blocks<G, U>(p, g, 0, g.nvb, 0, 1, EmitKey{keys});
+    stream_blocks<G, U, true>(p, g, 0, g.nvb, 0, 1, EmitKey{keys});
     wave_sync();
     select_row<false>(p, r, g, keys, ctl, area, 0, 1);
     wave_sync();
@@ -778,7 +801,7 @@ __global__ void __launch_bounds__(1024) select_group_rows_kernel(Params p) {
   for (int64_t r = blockIdx.x; r < p.items; r += gridDim.x) {
     const RowGeom g = row_geom(p, r, true);
     select_row_prepare(ctl, area, threadIdx.x, blockDim.x);
-    stream_blocks<G, kUnroll>(p, g, 0, g.nvb, wave, nw, EmitKey{smem});
+    stream_blocks<G, kUnroll, true>(p, g, 0, g.nvb, wave, nw, EmitKey{smem});
     __syncthreads();
     select_row<true>(p, r, g, smem, ctl, area, wave, nw);
     if (r + gridDim.x < p.items) __syncthreads();  // LDS is reused by the next row
@@ -799,7 +822,7 @@ __global__ void __launch_bounds__(kThreads) stream_keys_kernel(Params p) {
     const int32_t b0 = c * p.chunk_blocks;
     if (b0 >= g.nvb) continue;
     const int32_t b1 = b0 + p.chunk_blocks < g.nvb ? b0 + p.chunk_blocks : g.nvb;
-    stream_blocks<G, kUnroll>(p, g, b0, b1, wave, nw, EmitKey{p.ws_keys + r * p.nblocks});
+    stream_blocks<G, kUnroll, false>(p, g, b0, b1, wave, nw, EmitKey{p.ws_keys + r * p.nblocks});
   }
 }
 
@@ -849,7 +872,7 @@ __global__ void __launch_bounds__(kThreads) block_scores_kernel(Params p) {
     const int32_t b1 = b0 + p.chunk_blocks < p.nblocks ? b0 + p.chunk_blocks : p.nblocks;
     float* srow = p.scores + r * p.ld_scores;
     const int32_t sb1 = b1 < g.nvb ? b1 : g.nvb;
-    stream_blocks<G, kUnroll>(p, g, b0, sb1, wave, nw, EmitScore{srow, g.pin});
+    stream_blocks<G, kUnroll, false>(p, g, b0, sb1, wave, nw, EmitScore{srow, g.pin});
     const int32_t f0 = b0 > g.nvb ? b0 : g.nvb;
     for (int32_t b = f0 + (int32_t)threadIdx.x; b < b1; b += (int32_t)blockDim.x)
       srow[b] = b == g.pin ? __builtin_inff() : -__builtin_inff();
@@ -1234,10 +1257,12 @@ dsa_status_t dsa_select_plan(int64_t rows, int64_t width, int32_t block_size,
     // each, long rows a whole workgroup each.
     *plan = width <= 16384 ? kPlanWave : kPlanGroup;
     if (*plan == kPlanGroup) *plan_arg = kWaves;
-  } else if (rows >= 64 && width < 65536) {
-    // Decode batches of rows up to 256 KiB: one CU per row with up to 16
-    // waves streaming it, the select fused behind them (a single launch;
-    // measured faster than the split plan's two kernels for such rows).
+  } else if (rows >= 64 && rows * 1024 >= width) {
+    // Decode batches with enough rows to keep HBM busy one CU per row (64
+    // rows of 64K columns, 128 of 128K, 256 of 256K): up to 16 waves stream
+    // each row, the select fused behind them in the same launch.  Measured
+    // against the split plan's two kernels, the crossover sits near
+    // rows = width / 1024 for block sizes 64 and 128.
     *plan = kPlanGroup;
     *plan_arg = rows <= 256 ? 16 : (rows <= 512 ? 8 : kWaves);
   } else {

@@ -65,8 +65,11 @@ def test_auto_plan():
     assert B.select_plan(8192, 65536, 64, 64) == (1, 4)    # many long rows: a workgroup per row
     assert B.select_plan(8, 1000, 64, 4) == (3, 0)         # one chunk per row anyway
     assert B.select_plan(64, 32768, 64, 32) == (1, 16)     # decode: a 16-wave CU per row
-    assert B.select_plan(128, 131072, 128, 16) == (2, 64)  # long decode rows: 32 KiB chunks
-    assert B.select_plan(600, 131072, 128, 16) == (2, 256)  # 128 KiB chunks
+    assert B.select_plan(128, 131072, 128, 16) == (1, 16)  # long decode rows, enough of them
+    assert B.select_plan(96, 131072, 128, 16) == (2, 64)   # too few: 32 KiB chunks
+    assert B.select_plan(192, 262144, 64, 32) == (2, 384)
+    assert B.select_plan(256, 262144, 64, 32) == (1, 16)
+    assert B.select_plan(600, 131072, 128, 16) == (1, 4)
     assert B.select_plan(600, 32768, 64, 32) == (1, 4)
     p, cb = B.select_plan(16, 131072, 128, 16)             # very few long rows: split
     assert p == 2 and cb % 2 == 0 and cb >= 1
