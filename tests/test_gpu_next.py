@@ -72,6 +72,22 @@ def test_select_from_scores_full_size():
     assert np.array_equal(got, _oracle_sfs(w))
 
 
+@pytest.mark.parametrize("rows,k", [(200, 7), (700, 64), (3000, 64), (3000, 300)])
+def test_select_from_scores_row_counts(rows, k):
+    """The workgroup width follows the row count (16, 4 or 2 waves per row):
+    every width gives the oracle's ids, on scores with heavy ties, NaN, -inf,
+    rows whose global end is <= 0 and ends past the last block."""
+    rng = np.random.default_rng(rows + k)
+    nscore, G = 1024, 64
+    x = (np.rint(rng.uniform(-4, 4, size=(rows, nscore)) * 8) / 8).astype(np.float32)
+    x[rng.random((rows, nscore)) < 1e-3] = np.nan
+    x[rng.random((rows, nscore)) < 2e-2] = -np.inf
+    ends = rng.integers(-G, (nscore + 2) * G, size=rows).astype(np.int32)
+    w = workloads.ScoresWorkload(f"rows-{rows}-k{k}", x, ends, G, nscore, k, 1)
+    got = _gpu_sfs(w, ld_pad=rows % 3)
+    assert np.array_equal(got, _oracle_sfs(w))
+
+
 @pytest.mark.parametrize("W", [2, 4, 8])
 def test_dcp_decomposition_on_gpu(W):
     rng = np.random.default_rng(40 + W)
