@@ -134,11 +134,11 @@ dsa_status_t dsa_select_candidate_blocks(const float* logits, int64_t rows, int6
  * dsa_select_candidate_blocks with an explicit launch plan, for tests and
  * tuning.  Results are identical for every plan.
  *   plan          0: automatic (what dsa_select_candidate_blocks uses);
- *                 1: one workgroup per row (its waves stream the row, one
- *                    wave selects);
+ *                 1: one workgroup per row (its waves stream the row, then
+ *                    select it together);
  *                 2: split: a first kernel streams chunks of `plan_arg`
- *                    blocks of every row on many CUs into the workspace, a
- *                    second kernel selects, one wave per row;
+ *                    blocks of every row on many CUs into the workspace as
+ *                    keys, a second kernel selects, one workgroup per row;
  *                 3: one wave per row (stream and select), several rows per
  *                    workgroup.
  *   plan_arg      plan 1: waves per workgroup, 1..16 (0: 4);
