@@ -361,9 +361,10 @@ def test_all_equal_scores_take_lowest_ids():
 
 @pytest.mark.parametrize("plan", [1, 2, 3])
 def test_select_size_boundaries(plan):
-    """Rows whose candidate count sits on each side of the select's
-    register-slot boundaries (binary search up to 256 keys, radix above,
-    LDS-resident keys above 1024), with heavy ties and NaN/-inf."""
+    """Rows on each side of the select's size boundaries: the direct rank
+    (up to 64 blocks), one to several waves' worth of keys and candidates
+    (64, 128, 256, 512, 1024), and, with the heavy ties here, more than 256
+    candidates at the bound (the exact fallback); NaN and -inf rows too."""
     rng = np.random.default_rng(99)
     B = 4
     for n in (1, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 512, 513, 1023, 1024, 1025, 2000):
@@ -380,3 +381,36 @@ def test_select_size_boundaries(plan):
             got, sc = gpu_select(w, plan, 3)
             exp_out, exp_sc = oracle_select(w)
             assert_same(got, sc, exp_out, exp_sc, f"n={n} k={k} plan {plan}")
+
+
+@pytest.mark.parametrize("plan", [1, 2, 3])
+def test_select_at_lds_limit(plan):
+    """The largest row the LDS holds: 15312 blocks (15312 keys + 48 control
+    words + 1024 words of select area = 16384 words = 64 KiB); one block more
+    is rejected on the host (see test_abi_cpu)."""
+    rng = np.random.default_rng(plan)
+    nb, B, rows = 15312, 4, 3
+    width = nb * B
+    x = (np.rint(rng.standard_normal((rows, width)) * 8) / 8).astype(np.float32)
+    x[0, ::1000] = np.nan
+    ke = np.array([width, width // 3, 17], np.int32)
+    for k in (3, 200):
+        w = workloads.Workload(f"lds-limit-k{k}", x, None, ke, B, k, 1)
+        got, sc = gpu_select(w, plan, 1000 if plan == 2 else 0)
+        exp_out, exp_sc = oracle_select(w)
+        assert_same(got, sc, exp_out, exp_sc, f"lds limit k={k} plan {plan}")
+
+
+def test_more_rows_than_one_grid():
+    """More work items than one launch's grid (2^20 workgroups): the kernels
+    stride over the rest.  1.1M short rows, grouped 3 to a bound."""
+    rng = np.random.default_rng(5)
+    rows, width, B, k, R = 1_100_000, 16, 4, 2, 3
+    x = rng.integers(-8, 8, size=(rows, width)).astype(np.float32)
+    groups = -(-rows // R)
+    ke = rng.integers(0, width + 1, size=groups).astype(np.int32)
+    w = workloads.Workload("many-rows", x, None, ke, B, k, R)
+    exp_out, exp_sc = oracle_select(w)
+    for plan in (1, 3):
+        got, sc = gpu_select(w, plan)
+        assert_same(got, sc, exp_out, exp_sc, f"many rows plan {plan}")
