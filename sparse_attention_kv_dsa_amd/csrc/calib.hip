@@ -16,6 +16,13 @@ constexpr int64_t kMaxGrid = 1 << 20;
 // All three streams hand each workgroup whole 16 KiB items, one round of
 // four 16-byte accesses per thread: the shape that moved the most bytes per
 // second on this GPU among grid-stride and 8-64 KiB-per-workgroup variants.
+// Reads are nontemporal (8-10 % faster than cached reads here); stores are
+// plain (nontemporal stores were slower for the fill).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(r.x, r.y, r.z, r.w);
+}
 __global__ void __launch_bounds__(kThreads) copy_kernel(const uint4* __restrict__ src,
                                                         uint4* __restrict__ dst, int64_t n) {
   for (int64_t it = blockIdx.x; it * kItem < n; it += gridDim.x) {
@@ -24,7 +31,7 @@ __global__ void __launch_bounds__(kThreads) copy_kernel(const uint4* __restrict_
 #pragma unroll
     for (int j = 0; j < kUnits; ++j) {
       const int64_t i = b + j * kThreads;
-      v[j] = src[i < n ? i : n - 1];
+      v[j] = load_nt(src + (i < n ? i : n - 1));
     }
 #pragma unroll
     for (int j = 0; j < kUnits; ++j) {
@@ -43,7 +50,7 @@ __global__ void __launch_bounds__(kThreads) read_kernel(const uint4* __restrict_
 #pragma unroll
     for (int j = 0; j < kUnits; ++j) {
       const int64_t i = b + j * kThreads;
-      v[j] = src[i < n ? i : n - 1];
+      v[j] = load_nt(src + (i < n ? i : n - 1));
     }
 #pragma unroll
     for (int j = 0; j < kUnits; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
