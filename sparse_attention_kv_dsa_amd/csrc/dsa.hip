@@ -1270,12 +1270,14 @@ dsa_status_t dsa_select_plan(int64_t rows, int64_t width, int32_t block_size,
     if (*plan == kPlanGroup) *plan_arg = kWaves;
   } else if (rows >= 64 && rows * 1024 >= width) {
     // Decode batches with enough rows to keep HBM busy one CU per row (64
-    // rows of 64K columns, 128 of 128K, 256 of 256K): up to 16 waves stream
+    // rows of 64K columns, 128 of 128K, 256 of 256K): 8 or 16 waves stream
     // each row, the select fused behind them in the same launch.  Measured
     // against the split plan's two kernels, the crossover sits near
-    // rows = width / 1024 for block sizes 64 and 128.
+    // rows = width / 1024 for block sizes 64 and 128; 8 waves beat 16 on
+    // rows of up to 32K columns (a shorter select, two load rounds each),
+    // 16 win from 64K columns on.
     *plan = kPlanGroup;
-    *plan_arg = rows <= 256 ? 16 : (rows <= 512 ? 8 : kWaves);
+    *plan_arg = rows <= 256 ? (width <= 32768 ? 8 : 16) : (rows <= 512 ? 8 : kWaves);
   } else {
     // Few rows, or long rows: chunks of every row on all CUs, then a
     // selecting kernel (one CU streams only ~25-70 GB/s, so a row per CU

@@ -64,7 +64,8 @@ def test_auto_plan():
     assert B.select_plan(4096, 16384, 64, 32) == (3, 0)    # many short rows: a wave per row
     assert B.select_plan(8192, 65536, 64, 64) == (1, 4)    # many long rows: a workgroup per row
     assert B.select_plan(8, 1000, 64, 4) == (3, 0)         # one chunk per row anyway
-    assert B.select_plan(64, 32768, 64, 32) == (1, 16)     # decode: a 16-wave CU per row
+    assert B.select_plan(64, 32768, 64, 32) == (1, 8)      # decode: an 8-wave CU per row
+    assert B.select_plan(64, 65536, 64, 32) == (1, 16)     # longer rows: 16 waves
     assert B.select_plan(128, 131072, 128, 16) == (1, 16)  # long decode rows, enough of them
     assert B.select_plan(96, 131072, 128, 16) == (2, 64)   # too few: 32 KiB chunks
     assert B.select_plan(192, 262144, 64, 32) == (2, 384)
