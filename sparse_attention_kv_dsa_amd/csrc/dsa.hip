@@ -3,35 +3,40 @@
 // What is computed follows the vLLM-fork page
 // "launcher/dcp2/diffs/02-model_executor_kernels_attention_dsa_candidate_blocks.py.diff":
 // _max_with_nan (NaN-propagating max), _block_scores_kernel (masked window
-// load with -inf fill, newest-block pin), _block_scores, and the non-DCP
-// branch of _select_candidate_blocks_impl (early-outs, top-k, -1 padding).
-// The full contract is stated in include/dsa.h.
+// load with -inf fill, newest-block pin), _block_scores, the non-DCP branch
+// of _select_candidate_blocks_impl (early-outs, top-k, -1 padding), the DCP
+// branch's selection after its reduce, and the candidate masking after it;
+// and page 3 (sglang dcp kernels.py) for the log-sum-exp correction.  The
+// full contract is stated in include/dsa.h.
 //
 // How it is computed here (MI355X / CDNA4, wave64):
 //   * One HBM pass over the in-window logits.  A block of B = 4*G columns is
 //     G lanes of one float4 each; a wave instruction reads 1 KiB contiguous,
-//     every lane keeps kUnroll independent 16-byte loads in flight.
+//     every lane keeps kUnroll independent 16-byte loads in flight.  The
+//     loads are nontemporal (each logit is read once) and, where the block
+//     maxima go to LDS, roll: a tile's next load is issued as soon as the
+//     tile has been reduced.
 //   * The per-lane max of a float4 and the G-lane reduction use the IEEE-754-
 //     2019 maximum (v_maximum3_f32 on gfx950: NaN-propagating, -0 < +0);
 //     the lanes of a block are combined with DPP quad/row permutes inside a
 //     16-lane row, ds_swizzle across rows and a bpermute across halves.
 //   * Scores are kept as order-preserving uint32 keys (unsigned order ==
 //     float order, canonical NaN on top), in LDS for the select.
-//   * Top-k prunes, then ranks: the k-th largest of at most 64*gpl group
-//     maxima bounds the k-th largest key from below, the keys at or above it
-//     (the candidates) are compacted into LDS as distinct 64-bit words
-//     (key, inverted block id), and a candidate's output slot is the number
-//     of larger words.  Every wave of a row's workgroup takes part; rows with
-//     more candidates than the LDS holds fall back to an exact one-wave radix
-//     select.
+//   * Top-k prunes, then ranks: a lower bound on the k-th largest key (the
+//     k-th largest of 64 group maxima for k <= 32, radix passes over 8-bit
+//     digits above), then the keys at or above it (the candidates) are
+//     compacted into LDS as distinct 64-bit words (key, inverted block id),
+//     and a candidate's output slot is the number of larger words.  Every
+//     wave of a row's workgroup takes part; rows with more candidates than
+//     the LDS holds fall back to an exact one-wave radix select.
 //   * Launch plans: short rows take one wave per row (four rows per
-//     workgroup, no barrier at all); long rows take a workgroup whose waves
-//     stream the row into LDS and then select it together; few long rows
-//     (decode) are split in chunks over many CUs by a streaming kernel that
-//     writes the block keys, and a second kernel selects, one workgroup per
-//     row.  Cross-CU hand-off inside one kernel would need agent-scope
-//     fences, which on this chip write back and invalidate a whole XCD's L2
-//     each; the kernel boundary is the cheaper synchronisation.
+//     workgroup, no barrier at all); long rows, and decode batches with
+//     enough rows to keep HBM busy, take a workgroup per row whose waves
+//     stream the row into LDS and then select it together; a few long rows
+//     are split in chunks over many CUs by a streaming kernel that writes
+//     the block keys, and a second kernel selects, one workgroup per row.
+//     Cross-CU hand-off inside one kernel would need agent-scope fences or
+//     device-scope atomics, both measured slower than the kernel boundary.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -322,11 +327,12 @@ struct EmitScore {
 //
 // Top-k of one row's block keys, in four steps with no sort of the whole row:
 //  (A) every key becomes a rank key (-inf -> 0 "no candidate", -0 -> +0);
-//      aligned groups of lanes take their maximum, giving at most 64*gpl
-//      group maxima;
+//      group l of the 64 groups holds the keys i with i mod 64 == l, and
+//      each group takes its maximum;
 //  (C) T0 = the keff-th largest group maximum, keff = min(k, #nonzero keys).
 //      keff groups each hold a key >= T0, so T0 is a lower bound on the
-//      keff-th largest key: every selected key is >= T0;
+//      keff-th largest key: every selected key is >= T0.  For k > 32 the
+//      bound comes from radix passes instead (bound_radix);
 //  (E) the keys >= T0 (the candidates, few for any spread of values) are
 //      compacted into LDS as 64-bit words (rank key << 32 | ~block id), which
 //      are distinct and order exactly as the selection order (key descending,
