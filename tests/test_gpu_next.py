@@ -222,6 +222,20 @@ def test_lse_random(N):
         _check_lse(w.out, w.lses, rank, new, lse)
 
 
+@pytest.mark.parametrize("D", [4, 260, 1028, 1500])
+def test_lse_vector_lengths(D):
+    """D-vectors shorter than one pass, with a partial pass, and longer than
+    the part loaded ahead of the LSE math (1024 elements), for N <= 64 and
+    N > 64."""
+    for N in (3, 65):
+        w = workloads.lse_merge(B=3, H=2, D=D, N=N, seed=400 + D + N)
+        rank = N - 1
+        new, lse = dsa.correct_attn_out(torch.from_numpy(w.out).to(DEV),
+                                        torch.from_numpy(w.lses).to(DEV), rank)
+        torch.cuda.synchronize()
+        _check_lse(w.out, w.lses, rank, new, lse)
+
+
 def test_lse_strided_and_special_values():
     rng = np.random.default_rng(77)
     B, H, D, N = 6, 4, 64, 5
