@@ -416,8 +416,9 @@ def bench_next(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus N > 1 is not supported "
-                                   "(rows shard across GPUs with no communication, see DESIGN.md)"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus N > 1 is not "
+                                   "supported (rows would shard across GPUs with no "
+                                   "communication between them)"}))
         sys.exit(2)
     if args.op != "select":
         bench_next(args)
