@@ -555,6 +555,50 @@ __device__ __forceinline__ void select_row_prepare(uint32_t* ctl, uint32_t* area
   if (tid < kCtlWords) ctl[tid] = 0u;
 }
 
+// A lane's rank keys of one row, read from LDS once when the row has at most
+// kKeyRegs keys per lane, so the passes over the keys (counts, histograms,
+// compaction) work from registers instead of one dependent LDS read per key.
+// Iteration j of wave `wave` covers key i = wave*64 + j*nt + lane.  Only the
+// narrow workgroups of many-row selects (several keys per lane) gain: with
+// one key per lane the cache costs registers and occupancy, so kernels
+// choose it at compile time (KC).
+constexpr int kKeyRegs = 8;
+struct LaneKeys {
+  uint32_t v[kKeyRegs];
+  int32_t nj;   // iterations per lane (wave-uniform)
+  bool cached;  // nj <= kKeyRegs: v[0, nj) hold the keys
+};
+
+template <bool KC>
+__device__ __forceinline__ LaneKeys lane_keys(const uint32_t* keys, const RowGeom& g, int wave,
+                                              int nt) {
+  const int lane = threadIdx.x & 63;
+  const int32_t first = wave * 64;
+  LaneKeys lk;
+  lk.nj = g.nsel > first ? (g.nsel - first + nt - 1) / nt : 0;
+  lk.cached = KC && lk.nj <= kKeyRegs;
+#pragma unroll
+  for (int j = 0; j < kKeyRegs; ++j)  // all reads in flight at once
+    lk.v[j] = (lk.cached && j < lk.nj) ? select_rank_key(keys, g, first + j * nt + lane) : 0u;
+  return lk;
+}
+
+// Calls f(i, rank key of i) for this lane's keys, in iteration order (the
+// same order for every lane, so f may hold ballots).
+template <class F>
+__device__ __forceinline__ void for_lane_keys(const LaneKeys& lk, const uint32_t* keys,
+                                              const RowGeom& g, int wave, int nt, F&& f) {
+  const int lane = threadIdx.x & 63;
+  if (lk.cached) {
+#pragma unroll
+    for (int j = 0; j < kKeyRegs; ++j)
+      if (j < lk.nj) f(wave * 64 + j * nt + lane, lk.v[j]);  // wave-uniform
+  } else {
+    for (int32_t base = wave * 64; base < g.nsel; base += nt)  // wave-uniform
+      f(base + lane, select_rank_key(keys, g, base + lane));
+  }
+}
+
 // Candidate bound by radix passes, for larger k: 8-bit digits of the rank
 // keys from the top, one workgroup histogram per pass (LDS atomic adds, which
 // stay cheap under conflicts), wave 0 finds the digit bucket that holds the
@@ -569,19 +613,17 @@ constexpr int kCtlDone = 6;     // radix: bound final
 
 template <bool WG>
 __device__ __forceinline__ void bound_radix(const RowGeom& g, int32_t k, const uint32_t* keys,
-                                            uint32_t* ctl, uint32_t* hist, int wave, int nw) {
+                                            const LaneKeys& lk, uint32_t* ctl, uint32_t* hist,
+                                            int wave, int nw) {
   const int lane = threadIdx.x & 63;
   const int nt = nw * 64;
-  const int32_t nsel = g.nsel;
   uint32_t prefix = 0u, hmask = 0u;
   for (int shift = 24; shift >= 0; shift -= 8) {
     uint32_t nv = 0u;
-    for (int32_t base = wave * 64; base < nsel; base += nt) {  // wave-uniform
-      const int32_t i = base + lane;
-      const uint32_t rk = select_rank_key(keys, g, i);
+    for_lane_keys(lk, keys, g, wave, nt, [&](int32_t, uint32_t rk) {
       if (rk != 0u && (rk & hmask) == prefix) atomicAdd(&hist[(rk >> shift) & 255u], 1u);
       if (shift == 24) nv += (uint32_t)__popcll(__ballot(rk != 0u));
-    }
+    });
     if (shift == 24 && lane == 0 && nv != 0u) atomicAdd(&ctl[kCtlValid], nv);
     row_barrier<WG>();
     if (wave == 0) {
@@ -661,7 +703,7 @@ __device__ __forceinline__ uint32_t row_sum16(uint32_t v) {
 // the keys i with i mod 64 == l: T0 = the keff-th largest group maximum.
 // Same-address LDS max serialises per lane on this chip, so the maxima and
 // the bound go through per-wave LDS rows and slots, not atomics.
-template <bool WG, bool RADIX>
+template <bool WG, bool RADIX, bool KC>
 __device__ __forceinline__ void select_row_general(const Params& p, const RowGeom& g,
                                                    uint32_t* keys, uint32_t* ctl, uint32_t* area,
                                                    int32_t* out_row, int wave, int nw) {
@@ -671,20 +713,20 @@ __device__ __forceinline__ void select_row_general(const Params& p, const RowGeo
   const int32_t nsel = g.nsel, k = p.k;
   uint64_t* cand = reinterpret_cast<uint64_t*>(area);
   uint32_t t0, nvalid;
+  const LaneKeys lk = lane_keys<KC>(keys, g, wave, nt);
 
   if constexpr (RADIX) {
-    bound_radix<WG>(g, k, keys, ctl, area, wave, nw);
+    bound_radix<WG>(g, k, keys, lk, ctl, area, wave, nw);
     t0 = ctl[kCtlT0];
     nvalid = ctl[kCtlValid];
   } else {
     // (A) per lane: maximum of its keys (all in group `lane`), into this
     // wave's row of `area`; per wave: its count of nonzero keys.
     uint32_t tmax = 0u, nv = 0u;
-    for (int32_t base = wave * 64; base < nsel; base += nt) {  // wave-uniform
-      const uint32_t rk = select_rank_key(keys, g, base + lane);
+    for_lane_keys(lk, keys, g, wave, nt, [&](int32_t, uint32_t rk) {
       tmax = umax(tmax, rk);
       nv += (uint32_t)__popcll(__ballot(rk != 0u));
-    }
+    });
     area[wave * 64 + lane] = tmax;
     if (lane == 0) ctl[kCtlSlotCount + wave] = nv;
     row_barrier<WG>();
@@ -716,17 +758,40 @@ __device__ __forceinline__ void select_row_general(const Params& p, const RowGeo
   // (E) compact the candidates (keys >= T0) into LDS.
   {
     const uint32_t tt = t0 > 1u ? t0 : 1u;
-    for (int32_t base = wave * 64; base < nsel; base += nt) {  // wave-uniform
-      const int32_t i = base + lane;
-      const uint32_t rk = select_rank_key(keys, g, i);
-      const bool c = rk >= tt;
-      const uint64_t m = __ballot(c);
-      if (m != 0ull) {
+    if (KC && lk.cached) {
+      // every ballot first, then one atomic reserves all of this wave's slots
+      uint64_t m[kKeyRegs];
+      uint32_t tot = 0u;
+#pragma unroll
+      for (int j = 0; j < kKeyRegs; ++j) {
+        m[j] = __ballot(j < lk.nj && lk.v[j] >= tt);
+        tot += (uint32_t)__popcll(m[j]);
+      }
+      if (tot != 0u) {  // wave-uniform
         uint32_t b0 = 0u;
-        if (lane == 0) b0 = atomicAdd(&ctl[kCtlCand], (uint32_t)__popcll(m));
-        b0 = (uint32_t)__builtin_amdgcn_readlane((int)b0, 0);
-        const uint32_t pos = b0 + lanes_below(m);
-        if (c && pos < (uint32_t)kCandCap) cand[pos] = cand_word(rk, (uint32_t)i);
+        if (lane == 0) b0 = atomicAdd(&ctl[kCtlCand], tot);
+        uint32_t pos = (uint32_t)__builtin_amdgcn_readlane((int)b0, 0);
+#pragma unroll
+        for (int j = 0; j < kKeyRegs; ++j) {
+          const uint32_t at = pos + lanes_below(m[j]);
+          if (((m[j] >> lane) & 1ull) && at < (uint32_t)kCandCap)
+            cand[at] = cand_word(lk.v[j], (uint32_t)(wave * 64 + j * nt + lane));
+          pos += (uint32_t)__popcll(m[j]);
+        }
+      }
+    } else {
+      for (int32_t base = wave * 64; base < nsel; base += nt) {  // wave-uniform
+        const int32_t i = base + lane;
+        const uint32_t rk = select_rank_key(keys, g, i);
+        const bool c = rk >= tt;
+        const uint64_t m = __ballot(c);
+        if (m != 0ull) {
+          uint32_t b0 = 0u;
+          if (lane == 0) b0 = atomicAdd(&ctl[kCtlCand], (uint32_t)__popcll(m));
+          b0 = (uint32_t)__builtin_amdgcn_readlane((int)b0, 0);
+          const uint32_t pos = b0 + lanes_below(m);
+          if (c && pos < (uint32_t)kCandCap) cand[pos] = cand_word(rk, (uint32_t)i);
+        }
       }
     }
   }
@@ -752,7 +817,7 @@ __device__ __forceinline__ void select_row_general(const Params& p, const RowGeo
 // (16-byte aligned, max(kAreaMinWords, 2*kcap) words) are this row's LDS
 // scratch, cleared by select_row_prepare before the caller's last barrier.
 // Also writes the optional fp32 score row.
-template <bool WG>
+template <bool WG, bool KC = false>
 __device__ __forceinline__ void select_row(const Params& p, int64_t r, const RowGeom& g,
                                            uint32_t* keys, uint32_t* ctl, uint32_t* area,
                                            int wave, int nw) {
@@ -782,8 +847,8 @@ __device__ __forceinline__ void select_row(const Params& p, int64_t r, const Row
     }
     return;
   }
-  if (k <= 32) select_row_general<WG, false>(p, g, keys, ctl, area, out_row, wave, nw);
-  else select_row_general<WG, true>(p, g, keys, ctl, area, out_row, wave, nw);
+  if (k <= 32) select_row_general<WG, false, KC>(p, g, keys, ctl, area, out_row, wave, nw);
+  else select_row_general<WG, true, KC>(p, g, keys, ctl, area, out_row, wave, nw);
 }
 
 // Plan "wave": one wave per row, blockDim/64 rows per workgroup, no barrier.
@@ -940,7 +1005,7 @@ __global__ void __launch_bounds__(1024) select_scores_kernel(Params p) {
       }
     }
     __syncthreads();
-    select_row<true>(p, r, g, smem, ctl, area, wave, nw);
+    select_row<true, true>(p, r, g, smem, ctl, area, wave, nw);
     if (r + gridDim.x < p.items) __syncthreads();  // LDS is reused by the next row
   }
 }
