@@ -1012,7 +1012,7 @@ __global__ void __launch_bounds__(1024) select_scores_kernel(Params p) {
 
 // ------------------------------------------------------------- masking --
 
-constexpr int kMaskChunk = 8192;                    // columns per work item
+constexpr int kMaskChunk = 4096;                    // columns per work item (4K: measured best of 1K-32K)
 constexpr int kMaskBitWords = kMaskChunk / 32 + 2;  // blocks of one chunk, as bits
 
 struct MaskParams {
