@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
                     help="workload (1 tiny, 2 decode, 3 prefill, 4 long-context decode, 5 large prefill)")
-    ap.add_argument("--plan", type=int, default=0, choices=[0, 1, 2, 3])
+    ap.add_argument("--plan", type=int, default=0, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--plan-arg", type=int, default=0,
                     help="plan 1: waves per workgroup; plan 2: blocks per chunk (0: automatic)")
     ap.add_argument("--rotate-bytes", type=float, default=2.0, help="GiB of input copies to rotate over")
@@ -547,7 +547,8 @@ def main():
                      "algorithmic_bytes_per_launch": alg, "in_window_bytes": win,
                      "timed": "whole step (both kernels under the split plan)",
                      "kernel": {1: "select_group_rows_kernel", 2: "stream_keys_kernel",
-                                3: "select_wave_rows_kernel"}[plan]},
+                                3: "select_wave_rows_kernel",
+                                4: "select_pair_rows_kernel"}[plan]},
     }
 
     if not args.profile:

@@ -85,9 +85,11 @@ dsa_status_t dsa_block_scores(const float* logits, int64_t rows, int64_t width,
                               int64_t ld_scores, hipStream_t stream);
 
 /*
- * Bytes of device workspace the split plan of dsa_select_candidate_blocks
- * needs for this shape (one uint32 score key per row and block); enough for
- * every plan.  Pure host arithmetic; returns 0 for invalid or empty shapes.
+ * Bytes of device workspace the split and pair plans of
+ * dsa_select_candidate_blocks need for this shape: 2048 bytes of per-row
+ * arrival counters (pair plan, up to 256 rows), then one uint32 score key
+ * per row and block, rows padded to 32 keys.  Enough for every plan.  Pure
+ * host arithmetic; returns 0 for invalid or empty shapes.
  */
 size_t dsa_select_workspace_bytes(int64_t rows, int64_t width, int32_t block_size,
                                   int32_t topk_blocks);
@@ -104,11 +106,18 @@ size_t dsa_select_workspace_bytes(int64_t rows, int64_t width, int32_t block_siz
  *   scores_out  nullable fp32 [rows, ld_scores], ld_scores >= nblocks: the
  *               pinned block scores, for checking; ld_scores is ignored when
  *               scores_out is NULL.
- *   workspace   device scratch for the split plan (few long rows): at least
- *               dsa_select_workspace_bytes(...) bytes, 4-byte aligned,
- *               no initialisation needed.  Other plans do not touch it and
- *               it may then be NULL (dsa_select_plan tells the plan).  Calls
- *               that may run concurrently need separate workspaces.
+ *   workspace   device scratch for the split and pair plans (long rows):
+ *               at least dsa_select_workspace_bytes(...) bytes, 128-byte
+ *               aligned.  Its first 2048 bytes (the pair plan's arrival
+ *               counters) must be zero before the first call that uses it,
+ *               e.g. one hipMemset after allocation; every call that
+ *               completes leaves them zero again, and no other plan writes
+ *               them.  The rest needs no initialisation.  Other plans do
+ *               not touch the workspace.  When the automatic plan (what
+ *               dsa_select_plan names) needs one and none is given (NULL,
+ *               too small or misaligned), the call runs the group plan
+ *               instead.  Calls that may run concurrently need separate
+ *               workspaces.
  *
  * rows == 0 or topk_blocks == 0: DSA_OK, nothing written.
  * width == 0: out[r][j] = -1 for j < topk_blocks (page: the early exit of
@@ -140,10 +149,21 @@ dsa_status_t dsa_select_candidate_blocks(const float* logits, int64_t rows, int6
  *                    blocks of every row on many CUs into the workspace as
  *                    keys, a second kernel selects, one workgroup per row;
  *                 3: one wave per row (stream and select), several rows per
- *                    workgroup.
+ *                    workgroup;
+ *                 4: pair: several workgroups share a row, each streaming a
+ *                    range of its blocks and publishing its keys in the
+ *                    workspace; the last to arrive (per-row atomic counter)
+ *                    gathers the rest and selects.  A row's workgroups are
+ *                    dealt to one XCD so that the keys pass through its L2;
+ *                    a part that ran on another XCD is streamed again by the
+ *                    selecting workgroup.  At most 256 rows.
  *   plan_arg      plan 1: waves per workgroup, 1..16 (0: 4);
  *                 plan 2: blocks per chunk, >= 1 (0: automatic);
- *                 plan 3: float4 loads in flight per lane, 8 or 16 (0: 8).
+ *                 plan 3: float4 loads in flight per lane, 8 or 16 (0: 8);
+ *                 plan 4: waves | parts << 8 | spread << 16: waves per
+ *                    workgroup 0..16 and workgroups per row 0..255 (0:
+ *                    automatic), spread 1 deals a row's workgroups to
+ *                    different XCDs (for tests of the fallback).
  */
 dsa_status_t dsa_select_candidate_blocks_plan(
     const float* logits, int64_t rows, int64_t width, int64_t ld_logits,
@@ -152,7 +172,7 @@ dsa_status_t dsa_select_candidate_blocks_plan(
     void* workspace, size_t workspace_bytes, int32_t plan, int32_t plan_arg,
     hipStream_t stream);
 
-/* The automatic plan for a shape: *plan = 1, 2 or 3 and its *plan_arg. */
+/* The automatic plan for a shape: *plan = 1, 2, 3 or 4 and its *plan_arg. */
 dsa_status_t dsa_select_plan(int64_t rows, int64_t width, int32_t block_size,
                              int32_t topk_blocks, int32_t* plan, int32_t* plan_arg);
 

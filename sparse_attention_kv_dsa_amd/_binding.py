@@ -125,9 +125,11 @@ def select_plan(rows: int, width: int, block_size: int, topk_blocks: int) -> tup
 
 
 class Workspace:
-    """Device scratch for the split plan of dsa_select_candidate_blocks
-    (no initialisation needed; one per stream that may run concurrently).
-    Calls whose plan is another one get no default workspace."""
+    """Device scratch for the split and pair plans of
+    dsa_select_candidate_blocks: allocated zeroed (the pair plan's arrival
+    counters must start at zero; every call leaves them zero), one per stream
+    that may run concurrently.  Calls whose plan is another one get no
+    default workspace."""
 
     def __init__(self, device, nbytes: int = 0):
         self.device = torch.device(device)
@@ -198,12 +200,12 @@ def select_candidate_blocks(logits: torch.Tensor, row_ks: torch.Tensor | None,
             raise ValueError("scores_out must be float32 on the logits' device")
         ld_scores = _ld(scores_out)
     stream = _stream(logits.device)
-    # Only the split plan touches the workspace: no default one for the others.
+    # Only the split and pair plans touch the workspace: no default one for the others.
     chosen = plan
     if plan == 0 and rows >= 0 and width >= 0 and block_size > 0 and topk_blocks >= 0:
         chosen = select_plan(rows, width, block_size, topk_blocks)[0]
     ws_ptr, ws_bytes = None, 0
-    if chosen == 2 or workspace is not None:
+    if chosen in (2, 4) or workspace is not None:
         need = select_workspace_bytes(rows, width, block_size, topk_blocks) if block_size > 0 else 0
         if workspace is None:
             workspace = _default_workspace(logits.device, stream, need)

@@ -135,7 +135,11 @@ struct Params {
   int64_t ld_out;
   float* scores;  // block-scores output, or the optional write-back
   int64_t ld_scores;
-  uint32_t* ws_keys;  // split plan: [rows, nblocks] score keys
+  uint32_t* ws_keys;  // split and pair plans: [rows, ws_ld] score keys
+  int64_t ws_ld;      // row stride of ws_keys, a multiple of 32 (128-byte lines)
+  uint64_t* ws_count; // pair plan: per-row arrival counters, zero between calls
+  int32_t parts;      // pair plan: workgroups per row
+  int32_t spread;     // pair plan: a row's parts on consecutive workgroups (other XCDs)
   int64_t items;      // work items of the launch
 };
 
@@ -346,6 +350,7 @@ constexpr int kCtlWords = 48;       // per-row control words in LDS
 constexpr int kCtlValid = 0;        // #nonzero rank keys
 constexpr int kCtlCand = 1;         // #candidates (atomic add)
 constexpr int kCtlT0 = 2;           // candidate threshold
+constexpr int kCtlArrival = 8;      // pair plan: the row counter before this arrival (2 words)
 constexpr int kCtlSlotCount = 16;   // 16 per-wave slots: nonzero keys
 constexpr int kCtlSlotBound = 32;   // 16 per-wave slots: bound candidates
 constexpr int kCandCap = 256;   // candidates held in LDS (64-bit words)
@@ -904,7 +909,7 @@ __global__ void __launch_bounds__(kThreads) stream_keys_kernel(Params p) {
     const int32_t b0 = c * p.chunk_blocks;
     if (b0 >= g.nvb) continue;
     const int32_t b1 = b0 + p.chunk_blocks < g.nvb ? b0 + p.chunk_blocks : g.nvb;
-    stream_blocks<G, kUnroll, false>(p, g, b0, b1, wave, nw, EmitKey{p.ws_keys + r * p.nblocks});
+    stream_blocks<G, kUnroll, false>(p, g, b0, b1, wave, nw, EmitKey{p.ws_keys + r * p.ws_ld});
   }
 }
 
@@ -919,7 +924,7 @@ __global__ void __launch_bounds__(1024) select_keys_kernel(Params p) {
   for (int64_t r = blockIdx.x; r < p.items; r += gridDim.x) {
     const RowGeom g = row_geom(p, r, true);
     select_row_prepare(ctl, area, threadIdx.x, blockDim.x);
-    const uint32_t* src = p.ws_keys + r * p.nblocks;
+    const uint32_t* src = p.ws_keys + r * p.ws_ld;
     const int32_t nt = (int32_t)blockDim.x;
     for (int32_t b0 = 0; b0 < g.nvb; b0 += 4 * nt) {  // four loads in flight per lane
       uint32_t v[4];
@@ -938,6 +943,84 @@ __global__ void __launch_bounds__(1024) select_keys_kernel(Params p) {
     select_row<true>(p, r, g, smem, ctl, area, wave, nw);
     if (r + gridDim.x < p.items) __syncthreads();
   }
+}
+
+// Plan "pair": `parts` workgroups share a row.  Each streams one range of the
+// row's blocks (a whole number of 32-block key lines) into LDS, publishes its
+// keys in the workspace and counts itself in on the row's counter; the last
+// to arrive gathers the other ranges and selects the row.  Nobody waits, so
+// any residency works.  The gather reads the other workgroups' keys through
+// the L2 of its XCD: the hardware deals workgroups to the 8 XCDs round-robin,
+// so workgroup i runs on XCD i mod 8 and the grid puts a row's parts on one
+// XCD.  The counter records the XCD of every arrival (one 8-bit count per XCC
+// id); if a part ran elsewhere, its keys may sit in another XCD's L2, and the
+// last workgroup streams the other ranges again itself instead.  The last arrival
+// resets the counter to zero for the next call.  `spread` deals a row's parts
+// to consecutive workgroups instead, on different XCDs, which exercises that
+// fallback.
+__device__ __forceinline__ uint32_t xcc_id() {
+  // hwreg(HW_REG_XCC_ID, 0, 16): the XCC (XCD) this wave runs on
+  return (uint32_t)__builtin_amdgcn_s_getreg(20 | (0 << 6) | (15 << 11)) & 7u;
+}
+
+template <int G>
+__global__ void __launch_bounds__(1024) select_pair_rows_kernel(Params p) {
+  extern __shared__ uint32_t smem[];
+  const int wave = wave_index();
+  const int nw = blockDim.x >> 6;
+  const int tid = threadIdx.x;
+  const int nt = blockDim.x;
+  const int H = p.parts;
+  const int64_t j = p.spread ? blockIdx.x : blockIdx.x >> 3;
+  const int64_t r = p.spread ? j / H : (j / H) * 8 + (blockIdx.x & 7);
+  const int part = (int)(j % H);
+  if (r >= p.rows) return;
+  uint32_t* ctl = smem + p.keys_words;
+  uint32_t* area = ctl + kCtlWords;
+  uint64_t* s_old = reinterpret_cast<uint64_t*>(ctl + kCtlArrival);
+  const RowGeom g = row_geom(p, r, true);
+  select_row_prepare(ctl, area, tid, nt);
+  const int32_t cb = (((g.nvb + H - 1) / H) + 31) & ~31;
+  const int32_t b0 = part * cb < g.nvb ? part * cb : g.nvb;
+  const int32_t b1 = b0 + cb < g.nvb ? b0 + cb : g.nvb;
+  stream_blocks<G, kUnroll, true>(p, g, b0, b1, wave, nw, EmitKey{smem});
+  __syncthreads();
+  uint32_t* wrow = p.ws_keys + r * p.ws_ld;
+  for (int32_t b = b0 + tid; b < b1; b += nt) wrow[b] = smem[b];
+  // every key store acknowledged by L2 before the arrival is counted
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const uint32_t xcc = xcc_id();
+  if (tid == 0) *s_old = atomicAdd(reinterpret_cast<unsigned long long*>(p.ws_count + r),
+                                  1ull << (8 * xcc));
+  __syncthreads();
+  const uint64_t old = *s_old;
+  int arrived = 0;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) arrived += (int)((old >> (8 * x)) & 255u);
+  if (arrived != H - 1) return;
+  if (tid == 0) atomicExch(reinterpret_cast<unsigned long long*>(p.ws_count + r), 0ull);
+  if ((int)((old >> (8 * xcc)) & 255u) == H - 1) {
+    // every other part published its keys in this XCD's L2
+    for (int32_t c0 = 0; c0 < g.nvb; c0 += 4 * nt) {
+      uint32_t v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int32_t b = c0 + q * nt + tid;
+        v[q] = (b < g.nvb && (b < b0 || b >= b1)) ? wrow[b] : 0u;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int32_t b = c0 + q * nt + tid;
+        if (b < g.nvb && (b < b0 || b >= b1)) smem[b] = v[q];
+      }
+    }
+  } else {
+    stream_blocks<G, kUnroll, true>(p, g, 0, b0, wave, nw, EmitKey{smem});
+    stream_blocks<G, kUnroll, true>(p, g, b1, g.nvb, wave, nw, EmitKey{smem});
+  }
+  __syncthreads();
+  select_row<true>(p, r, g, smem, ctl, area, wave, nw);
 }
 
 // Block scores to HBM; item = r * nchunks + c covers blocks
@@ -1243,6 +1326,7 @@ DSA_WAVE_TABLE(8)
 DSA_WAVE_TABLE(16)
 DSA_KERNEL_TABLE(select_group_rows_kernel)
 DSA_KERNEL_TABLE(stream_keys_kernel)
+DSA_KERNEL_TABLE(select_pair_rows_kernel)
 DSA_KERNEL_TABLE(block_scores_kernel)
 
 // Launches `fn` over `items` work items with `threads` per workgroup and
@@ -1285,7 +1369,15 @@ int64_t select_wave_words(int64_t nblocks, int32_t k) {
 }
 
 // Plan ids (also the values of dsa_select_candidate_blocks_plan's `plan`).
-enum { kPlanGroup = 1, kPlanSplit = 2, kPlanWave = 3 };
+enum { kPlanGroup = 1, kPlanSplit = 2, kPlanWave = 3, kPlanPair = 4 };
+
+// Workspace layout: per-row arrival counters of the pair plan (zero between
+// calls), then the score keys of the split and pair plans, rows 128-byte
+// aligned.
+constexpr int64_t kCountRows = 256;
+constexpr size_t kCountBytes = kCountRows * 8;
+constexpr uintptr_t kWsAlign = 128;
+int64_t ws_row_words(int64_t nblocks) { return cdiv(nblocks, 32) * 32; }
 
 // Chunk size for split rows: aim at ~2048 workgroups in total, 8K-32K columns
 // each, and a multiple of the blocks one wave instruction covers.
@@ -1302,6 +1394,17 @@ int32_t auto_chunk_blocks(int64_t rows, int64_t width, int32_t B) {
   if (cb < 1) cb = 1;
   if (cb > 0x3FFFFFFF) cb = 0x3FFFFFFF;
   return (int32_t)cb;
+}
+
+// Pair plan shape for `rows` rows of `width` columns: workgroups per row
+// (fill the 256 CUs about once, at most 8) and waves per workgroup (16 once
+// each part is long: from 32K columns a part for 4 and 8 parts, from 128K for
+// 2 parts; measured on decode shapes of 8-128 rows and 32K-256K columns).
+void pair_shape(int64_t rows, int64_t width, int* parts, int* waves) {
+  const int64_t r8 = cdiv(rows, 8) * 8;
+  *parts = r8 <= 32 ? 8 : (r8 <= 64 ? 4 : 2);
+  const int64_t long_part = *parts == 2 ? 262144 : 32768 * (int64_t)*parts;
+  *waves = width >= long_part ? 16 : 8;
 }
 
 }  // namespace
@@ -1323,7 +1426,7 @@ size_t dsa_select_workspace_bytes(int64_t rows, int64_t width, int32_t block_siz
                                   int32_t topk_blocks) {
   if (rows <= 0 || width <= 0 || block_size < 1 || topk_blocks < 0) return 0;
   const int64_t nblocks = cdiv(width, block_size);
-  return (size_t)rows * (size_t)nblocks * 4u;
+  return kCountBytes + (size_t)rows * (size_t)ws_row_words(nblocks) * 4u;
 }
 
 dsa_status_t dsa_select_plan(int64_t rows, int64_t width, int32_t block_size,
@@ -1339,14 +1442,23 @@ dsa_status_t dsa_select_plan(int64_t rows, int64_t width, int32_t block_size,
     // each, long rows a whole workgroup each.
     *plan = width <= 16384 ? kPlanWave : kPlanGroup;
     if (*plan == kPlanGroup) *plan_arg = kWaves;
-  } else if (rows >= 64 && rows * 1024 >= width) {
-    // Decode batches with enough rows to keep HBM busy one CU per row (64
-    // rows of 64K columns, 128 of 128K, 256 of 256K): 8 or 16 waves stream
-    // each row, the select fused behind them in the same launch.  Measured
-    // against the split plan's two kernels, the crossover sits near
-    // rows = width / 1024 for block sizes 64 and 128; 8 waves beat 16 on
-    // rows of up to 32K columns (a shorter select, two load rounds each),
-    // 16 win from 64K columns on.
+  } else if (rows <= 128 && width >= 32768) {
+    // Decode batches of up to 128 rows of 32K columns or more: 2-8
+    // workgroups share each row (the pair plan), so that every CU streams;
+    // it beat the one-workgroup-per-row and split plans on every such shape
+    // measured (8-128 rows, 32K-256K columns, block sizes 64 and 128).
+    int parts, waves;
+    pair_shape(rows, width, &parts, &waves);
+    *plan = kPlanPair;
+    *plan_arg = waves | parts << 8;
+  } else if (rows * 1024 >= width || width <= 32768) {
+    // Rows of up to 32K columns, or enough rows to keep HBM busy one CU per
+    // row (256 rows of 256K columns): 8 or 16 waves stream each row, the
+    // select fused behind them in the same launch.  Measured against the
+    // split plan's two kernels, the crossover sits near rows = width / 1024
+    // for block sizes 64 and 128; 8 waves beat 16 on rows of up to 32K
+    // columns (a shorter select, two load rounds each), 16 win from 64K
+    // columns on.
     *plan = kPlanGroup;
     *plan_arg = rows <= 256 ? (width <= 32768 ? 8 : 16) : (rows <= 512 ? 8 : kWaves);
   } else {
@@ -1406,8 +1518,10 @@ dsa_status_t dsa_select_candidate_blocks_plan(
     hipStream_t stream) {
   if (rows < 0 || width < 0 || block_size < 1 || row_repeat < 1 || topk_blocks < 0)
     return DSA_ERR_INVALID_ARG;
-  if (plan < 0 || plan > 3 || plan_arg < 0) return DSA_ERR_INVALID_ARG;
+  if (plan < 0 || plan > 4 || plan_arg < 0) return DSA_ERR_INVALID_ARG;
   if (plan == kPlanGroup && plan_arg > 16) return DSA_ERR_INVALID_ARG;
+  if (plan == kPlanPair && ((plan_arg & 255) > 16 || (plan_arg >> 16) > 1))
+    return DSA_ERR_INVALID_ARG;
   if (plan == kPlanWave && plan_arg != 0 && plan_arg != 8 && plan_arg != 16)
     return DSA_ERR_INVALID_ARG;
   if (ld_logits < width || ld_out < topk_blocks) return DSA_ERR_INVALID_ARG;
@@ -1430,13 +1544,19 @@ dsa_status_t dsa_select_candidate_blocks_plan(
   const int64_t ww = select_wave_words(nblocks, topk_blocks);
   if (ww * 4 > (int64_t)kLdsLimit) return DSA_ERR_UNSUPPORTED;
 
-  if (plan == 0) dsa_select_plan(rows, width, block_size, topk_blocks, &plan, &plan_arg);
-  if (plan == kPlanSplit) {
-    if (plan_arg == 0) plan_arg = auto_chunk_blocks(rows, width, block_size);
-    const size_t need = dsa_select_workspace_bytes(rows, width, block_size, topk_blocks);
-    if (!workspace || workspace_bytes < need || misaligned(workspace, 4))
-      return DSA_ERR_WORKSPACE;
+  const size_t ws_need = dsa_select_workspace_bytes(rows, width, block_size, topk_blocks);
+  const bool ws_ok = workspace && workspace_bytes >= ws_need && !misaligned(workspace, kWsAlign);
+  if (plan == 0) {
+    dsa_select_plan(rows, width, block_size, topk_blocks, &plan, &plan_arg);
+    if ((plan == kPlanSplit || plan == kPlanPair) && !ws_ok) {
+      // no usable workspace: the plan that needs none
+      plan = kPlanGroup;
+      plan_arg = width <= 32768 ? 8 : 16;
+    }
   }
+  if (plan == kPlanSplit && plan_arg == 0) plan_arg = auto_chunk_blocks(rows, width, block_size);
+  if (plan == kPlanPair && rows > kCountRows) return DSA_ERR_UNSUPPORTED;
+  if ((plan == kPlanSplit || plan == kPlanPair) && !ws_ok) return DSA_ERR_WORKSPACE;
 
   Params p = {};
   p.logits = logits;
@@ -1458,7 +1578,11 @@ dsa_status_t dsa_select_candidate_blocks_plan(
   p.ld_out = ld_out;
   p.scores = scores_out;
   p.ld_scores = ld_scores;
-  p.ws_keys = static_cast<uint32_t*>(workspace);
+  if (workspace) {
+    p.ws_count = static_cast<uint64_t*>(workspace);
+    p.ws_keys = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + kCountBytes);
+    p.ws_ld = ws_row_words(nblocks);
+  }
   const int g = lanes_per_block(block_size);
   // waves per workgroup for the one-wave-per-row kernels: as many row states
   // as fit in LDS, up to four
@@ -1471,6 +1595,16 @@ dsa_status_t dsa_select_candidate_blocks_plan(
   if (plan == kPlanGroup) {
     const int waves = plan_arg > 0 ? plan_arg : kWaves;
     return launch(select_group_rows_kernel_ptr(g), rows, 64 * waves, 1, (size_t)ww * 4, stream, p);
+  }
+  if (plan == kPlanPair) {
+    int parts, waves;
+    pair_shape(rows, width, &parts, &waves);
+    if ((plan_arg >> 8) & 255) parts = (plan_arg >> 8) & 255;
+    if (plan_arg & 255) waves = plan_arg & 255;
+    p.parts = parts;
+    p.spread = plan_arg >> 16;
+    return launch(select_pair_rows_kernel_ptr(g), 8 * parts * cdiv(rows, 8), 64 * waves, 1,
+                  (size_t)ww * 4, stream, p);
   }
   p.chunk_blocks = plan_arg < p.nblocks ? plan_arg : p.nblocks;
   p.nchunks = (int32_t)cdiv(nblocks, p.chunk_blocks);

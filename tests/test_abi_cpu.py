@@ -52,8 +52,10 @@ def test_status_strings():
 def test_workspace_bytes():
     L = B.lib()
     # one uint32 key per row and block
-    assert L.dsa_select_workspace_bytes(64, 32768, 64, 32) == 64 * 512 * 4
-    assert L.dsa_select_workspace_bytes(65, 100, 7, 3) == 65 * 15 * 4
+    # 2 KiB of pair-plan arrival counters, then rows of keys padded to 32
+    assert L.dsa_select_workspace_bytes(64, 32768, 64, 32) == 2048 + 64 * 512 * 4
+    assert L.dsa_select_workspace_bytes(65, 100, 7, 3) == 2048 + 65 * 32 * 4
+    assert L.dsa_select_workspace_bytes(3, 100000, 64, 3) == 2048 + 3 * 1568 * 4
     assert L.dsa_select_workspace_bytes(0, 100, 7, 3) == 0
     assert L.dsa_select_workspace_bytes(5, 0, 7, 3) == 0
     assert L.dsa_select_workspace_bytes(5, 100, 0, 3) == 0
@@ -64,15 +66,25 @@ def test_auto_plan():
     assert B.select_plan(4096, 16384, 64, 32) == (3, 0)    # many short rows: a wave per row
     assert B.select_plan(8192, 65536, 64, 64) == (1, 4)    # many long rows: a workgroup per row
     assert B.select_plan(8, 1000, 64, 4) == (3, 0)         # one chunk per row anyway
-    assert B.select_plan(64, 32768, 64, 32) == (1, 8)      # decode: an 8-wave CU per row
-    assert B.select_plan(64, 65536, 64, 32) == (1, 16)     # longer rows: 16 waves
-    assert B.select_plan(128, 131072, 128, 16) == (1, 16)  # long decode rows, enough of them
-    assert B.select_plan(96, 131072, 128, 16) == (2, 64)   # too few: 32 KiB chunks
-    assert B.select_plan(192, 262144, 64, 32) == (2, 384)
+    # decode batches of up to 128 rows of >= 32K columns: the pair plan,
+    # plan_arg = waves | parts << 8
+    assert B.select_plan(64, 32768, 64, 32) == (4, 8 | 4 << 8)
+    assert B.select_plan(64, 65536, 64, 32) == (4, 8 | 4 << 8)
+    assert B.select_plan(64, 131072, 64, 32) == (4, 16 | 4 << 8)
+    assert B.select_plan(128, 131072, 128, 16) == (4, 8 | 2 << 8)
+    assert B.select_plan(96, 262144, 128, 16) == (4, 16 | 2 << 8)
+    assert B.select_plan(16, 131072, 128, 16) == (4, 8 | 8 << 8)
+    assert B.select_plan(1, 262144, 128, 16) == (4, 16 | 8 << 8)
+    # shorter rows: one workgroup per row, also for few rows
+    assert B.select_plan(8, 16384, 64, 32) == (1, 8)
+    assert B.select_plan(128, 16384, 64, 32) == (1, 8)
+    assert B.select_plan(192, 65536, 64, 32) == (1, 16)
     assert B.select_plan(256, 262144, 64, 32) == (1, 16)
     assert B.select_plan(600, 131072, 128, 16) == (1, 4)
     assert B.select_plan(600, 32768, 64, 32) == (1, 4)
-    p, cb = B.select_plan(16, 131072, 128, 16)             # very few long rows: split
+    # more than 128 rows, too few for their length: split
+    assert B.select_plan(192, 262144, 64, 32) == (2, 384)
+    p, cb = B.select_plan(300, 1 << 20, 128, 16)
     assert p == 2 and cb % 2 == 0 and cb >= 1
 
 
@@ -88,13 +100,17 @@ def _sel(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(rows=-1), 1), (dict(width=-1), 1), (dict(B=0), 1), (dict(R=0), 1), (dict(k=-1), 1),
-    (dict(ld=63), 1), (dict(ld_out=3), 1), (dict(plan=4), 1), (dict(plan=-1), 1), (dict(cb=-1), 1),
+    (dict(ld=63), 1), (dict(ld_out=3), 1), (dict(plan=5), 1), (dict(plan=-1), 1), (dict(cb=-1), 1),
     (dict(plan=1, cb=17), 1), (dict(plan=3, cb=4), 1),
     (dict(scores=FAKE, ld_scores=7), 1),         # nblocks = 8
     (dict(out=None), 1), (dict(out=FAKE2 + 2), 1), (dict(logits=None), 1), (dict(ke=None), 1),
     (dict(logits=FAKE + 2), 1), (dict(scores=FAKE + 1, ld_scores=8), 1),
     (dict(ws=None, plan=2), 3), (dict(ws_bytes=100, plan=2), 3), (dict(ws=FAKE + 2, plan=2), 3),
-    (dict(ws=None, plan=2, cb=3), 3),
+    (dict(ws=None, plan=2, cb=3), 3), (dict(ws=FAKE + 64, plan=2), 3),
+    (dict(plan=4, cb=17), 1), (dict(plan=4, cb=2 << 16), 1),
+    (dict(plan=4, ws=None), 3),
+    (dict(plan=4, ws_bytes=2047), 3), (dict(plan=4, ws=FAKE + 64), 3),
+    (dict(plan=4, rows=257), 2),                                     # 256 arrival counters
     (dict(width=1 << 20, ld=1 << 20, B=16, k=4096, ld_out=4096), 2),  # keys do not fit in LDS
     (dict(width=15312 * 4 + 4, ld=1 << 16, B=4, k=3, ld_out=3), 2),   # 15316 + 48 + 1024 words > 16384
     (dict(width=15312 * 4, ld=1 << 16, B=4, k=3, ld_out=3, plan=2, ws=None), 3),  # 15312 + 48 + 1024 fits
@@ -102,6 +118,18 @@ def _sel(**kw):
 ])
 def test_select_rejects_on_host(kw, code):
     assert _sel(**kw) == code
+
+
+def test_auto_plan_without_workspace_takes_the_group_plan():
+    """A pair-plan shape with no (or a too small or misaligned) workspace is
+    not rejected under the automatic plan: it passes every host check and
+    reaches the launch (DSA_ERR_HIP = 4 here, with no GPU), while the
+    explicit pair plan reports DSA_ERR_WORKSPACE."""
+    shape = dict(rows=64, width=32768, ld=32768, B=64, k=32, ld_out=32)
+    assert B.select_plan(64, 32768, 64, 32)[0] == 4
+    for ws in (dict(ws=None), dict(ws_bytes=100), dict(ws=FAKE + 64)):
+        assert _sel(**shape, **ws) == 4
+        assert _sel(**shape, **ws, plan=4) == 3
 
 
 def _bs(**kw):

@@ -45,7 +45,7 @@ def _i32(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
 
 
-@pytest.mark.parametrize("cfg,plan", [(2, 0), (2, 2), (4, 0), (3, 0), (1, 3)])
+@pytest.mark.parametrize("cfg,plan", [(2, 0), (2, 2), (4, 0), (3, 0), (1, 3), (4, 4), (2, 4)])
 def test_select_in_graph(cfg, plan):
     w = workloads.config(cfg)
     x = torch.from_numpy(w.logits).to(DEV)

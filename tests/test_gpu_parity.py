@@ -38,12 +38,22 @@ def dev_i32(a):
     return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
 
 
+def pair_arg(cb: int) -> int:
+    """An assorted pair-plan argument: waves | parts << 8 | spread << 16."""
+    waves = (0, 1, 4, 16)[cb % 4]
+    parts = (0, 2, 3, 8, 1, 32)[cb % 6]
+    return waves | parts << 8 | ((cb // 3) % 2) << 16
+
+
 def gpu_select(w, plan=0, cb=0, ld_pad=0, offset=0, with_scores=True, ld_out_pad=0):
-    """cb: the plan argument (plan 1: waves per workgroup, plan 2: blocks per chunk)."""
+    """cb: the plan argument (plan 1: waves per workgroup, plan 2: blocks per
+    chunk; plans 3 and 4 map it onto their own arguments)."""
     if plan == 1 and cb:
         cb = 1 + (cb - 1) % 16
     if plan == 3:
         cb = 16 if cb % 2 else 8
+    if plan == 4:
+        cb = pair_arg(cb)
     x = dev_logits(w.logits, ld_pad, offset)
     nb = -(-w.width // w.block_size)
     out_full = torch.full((w.rows, w.topk_blocks + ld_out_pad), 12345, dtype=torch.int32, device=DEV)
@@ -113,7 +123,8 @@ def _golden_workload(c):
                               c["topk"], c["row_repeat"])
 
 
-@pytest.mark.parametrize("plan,cb", [(1, 0), (1, 1), (1, 16), (2, 1), (2, 2), (3, 0), (3, 1)])
+@pytest.mark.parametrize("plan,cb", [(1, 0), (1, 1), (1, 16), (2, 1), (2, 2), (3, 0), (3, 1),
+                                     (4, 0), (4, 1), (4, 3), (4, 5), (4, 7)])
 def test_hand_worked_rows(plan, cb):
     for c in _golden():
         w = _golden_workload(c)
@@ -123,7 +134,7 @@ def test_hand_worked_rows(plan, cb):
         assert_same(got, sc, exp_out, exp_sc, c["id"])
 
 
-@pytest.mark.parametrize("plan", [1, 2, 3])
+@pytest.mark.parametrize("plan", [1, 2, 3, 4])
 def test_random_tiny_cases(plan):
     """400 tiny cases: NaN, +-0, +-inf, ties, odd widths and block sizes,
     negative/overlong/empty windows, row_repeat 1-3, k 0-12."""
@@ -138,7 +149,7 @@ def test_random_tiny_cases(plan):
 MEDIUM_B = [1, 3, 4, 5, 8, 12, 16, 32, 64, 100, 128, 256, 512]
 
 
-@pytest.mark.parametrize("plan", [1, 2, 3])
+@pytest.mark.parametrize("plan", [1, 2, 3, 4])
 def test_random_medium_cases(plan):
     """Several tiles per row and ragged tails, aligned (vector) and unaligned
     (scalar) rows, both launch plans with assorted chunk sizes."""
@@ -214,9 +225,13 @@ def test_config_full(cfg):
     assert_same(got, sc, exp_out, exp_sc, w.name)
     # the other plans give the same bits
     auto = dsa.select_plan(w.rows, w.width, w.block_size, w.topk_blocks)[0]
-    for plan in {1, 2, 3} - {auto}:
+    for plan in sorted({1, 2, 3} - {auto}):
         got2, sc2 = gpu_select(w, plan=plan)
         assert_same(got2, sc2, exp_out, exp_sc, f"{w.name} plan {plan}")
+    if w.rows <= 256:
+        for cb in range(6):   # pair plan: parts on one XCD and spread over XCDs
+            got2, sc2 = gpu_select(w, plan=4, cb=cb)
+            assert_same(got2, sc2, exp_out, exp_sc, f"{w.name} plan 4 arg {pair_arg(cb):#x}")
 
 
 def _check_properties(out, nblocks):
@@ -297,7 +312,8 @@ def test_repeat_calls_bit_identical():
     ks, ke = dev_i32(w.row_ks), dev_i32(w.row_ke)
     ws = dsa.Workspace(DEV)
     first = None
-    for plan, cb in ((2, 0), (2, 4), (1, 0), (1, 16), (3, 0), (3, 16)):
+    for plan, cb in ((2, 0), (2, 4), (1, 0), (1, 16), (3, 0), (3, 16), (4, 0), (4, 8 | 4 << 8),
+                     (4, 1 << 16)):
         for _ in range(50):
             out = torch.empty((w.rows, w.topk_blocks), dtype=torch.int32, device=DEV)
             dsa.select_candidate_blocks(x, ks, ke, w.topk_blocks, w.block_size, out, w.row_repeat,
@@ -342,7 +358,7 @@ def test_large_k_and_full_sort():
         x = np.round(rng.standard_normal((6, width)).astype(np.float32) * 4) / 4
         ke = rng.integers(0, width + 1, size=6).astype(np.int32)
         w = workloads.Workload(f"k{k}", x, None, ke, B, k, 1)
-        for plan in (1, 2, 3):
+        for plan in (1, 2, 3, 4):
             got, sc = gpu_select(w, plan, 7)
             exp_out, exp_sc = oracle_select(w)
             assert_same(got, sc, exp_out, exp_sc, f"k={k} plan {plan}")
@@ -359,7 +375,7 @@ def test_all_equal_scores_take_lowest_ids():
     assert np.array_equal(got, exp_out)
 
 
-@pytest.mark.parametrize("plan", [1, 2, 3])
+@pytest.mark.parametrize("plan", [1, 2, 3, 4])
 def test_select_size_boundaries(plan):
     """Rows on each side of the select's size boundaries: the direct rank
     (up to 64 blocks), one to several waves' worth of keys and candidates
@@ -383,7 +399,7 @@ def test_select_size_boundaries(plan):
             assert_same(got, sc, exp_out, exp_sc, f"n={n} k={k} plan {plan}")
 
 
-@pytest.mark.parametrize("plan", [1, 2, 3])
+@pytest.mark.parametrize("plan", [1, 2, 3, 4])
 def test_select_at_lds_limit(plan):
     """The largest row the LDS holds: 15312 blocks (15312 keys + 48 control
     words + 1024 words of select area = 16384 words = 64 KiB); one block more
@@ -396,7 +412,7 @@ def test_select_at_lds_limit(plan):
     ke = np.array([width, width // 3, 17], np.int32)
     for k in (3, 200):
         w = workloads.Workload(f"lds-limit-k{k}", x, None, ke, B, k, 1)
-        got, sc = gpu_select(w, plan, 1000 if plan == 2 else 0)
+        got, sc = gpu_select(w, plan, {2: 1000, 4: 3}.get(plan, 0))
         exp_out, exp_sc = oracle_select(w)
         assert_same(got, sc, exp_out, exp_sc, f"lds limit k={k} plan {plan}")
 
