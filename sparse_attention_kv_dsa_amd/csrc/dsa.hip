@@ -32,11 +32,15 @@
 //   * Launch plans: short rows take one wave per row (four rows per
 //     workgroup, no barrier at all); long rows, and decode batches with
 //     enough rows to keep HBM busy, take a workgroup per row whose waves
-//     stream the row into LDS and then select it together; a few long rows
-//     are split in chunks over many CUs by a streaming kernel that writes
-//     the block keys, and a second kernel selects, one workgroup per row.
-//     Cross-CU hand-off inside one kernel would need agent-scope fences or
-//     device-scope atomics, both measured slower than the kernel boundary.
+//     stream the row into LDS and then select it together; decode batches
+//     of up to 128 long rows share each row among 2-8 workgroups of one XCD,
+//     which hand their keys to the last of them through that XCD's L2 (a
+//     per-row arrival counter, no waiting); more rows, too few for their
+//     length, are split in chunks over many CUs by a streaming kernel that
+//     writes the block keys, and a second kernel selects, one workgroup per
+//     row.  A hand-off through memory instead (agent-scope fences, or
+//     device-scope stores and loads) measured slower than the kernel
+//     boundary.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
