@@ -159,21 +159,33 @@ struct RowGeom {
   int32_t nsel;   // blocks [0, nsel) can be candidates
 };
 
+// n / d for 0 <= n < 2^33 and 1 <= d < 2^31: the 32-bit divide when n fits.
+__device__ __forceinline__ int64_t div_bound(int64_t n, int32_t d) {
+  if ((n >> 32) == 0) return (int64_t)((uint32_t)n / (uint32_t)d);
+  return n / d;
+}
+
+// Called by every lane of a wave (uniform control flow).
 __device__ __forceinline__ RowGeom row_geom(const Params& p, int64_t r, bool pin) {
   RowGeom g;
-  int64_t grp = r / p.R;
-  g.s = p.ks ? (int64_t)p.ks[grp] : 0;
-  int64_t e = (int64_t)p.ke[grp];
+  // rows < 2^31: a 32-bit divide, none for row_repeat 1
+  const int64_t grp = p.R == 1 ? r : (int64_t)((uint32_t)r / (uint32_t)p.R);
+  // one load brings both bounds (lane 0: the start, the others: the end),
+  // one memory round trip instead of two; every lane of the wave is active
+  const int32_t* bp = ((threadIdx.x & 63) == 0 && p.ks) ? p.ks + grp : p.ke + grp;
+  const int32_t bv = *bp;
+  g.s = p.ks ? (int64_t)__builtin_amdgcn_readlane(bv, 0) : 0;
+  const int64_t e = (int64_t)__builtin_amdgcn_readlane(bv, 1);
   g.row = p.logits + r * p.ld;
   g.lo = g.s > 0 ? g.s : 0;
   g.hi = e < p.width ? e : p.width;
   int64_t nvb = 0;
-  if (g.hi > g.lo) nvb = (g.hi - g.s + p.B - 1) / p.B;
+  if (g.hi > g.lo) nvb = div_bound(g.hi - g.s + p.B - 1, p.B);
   if (nvb > p.nblocks) nvb = p.nblocks;
   g.nvb = (int32_t)nvb;
   g.pin = -1;
   if (pin && e > g.s) {
-    int64_t q = (e - g.s - 1) / p.B;
+    const int64_t q = div_bound(e - g.s - 1, p.B);
     if (q < p.nblocks) g.pin = (int32_t)q;
   }
   g.nsel = g.nvb > g.pin + 1 ? g.nvb : g.pin + 1;
