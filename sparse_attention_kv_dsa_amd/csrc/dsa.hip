@@ -961,10 +961,10 @@ __global__ void __launch_bounds__(1024) select_keys_kernel(Params p) {
   }
 }
 
-// Plan "pair": `parts` workgroups share a row.  Each streams one range of the
-// row's blocks (a whole number of 32-block key lines) into LDS, publishes its
-// keys in the workspace and counts itself in on the row's counter; the last
-// to arrive gathers the other ranges and selects the row.  Nobody waits, so
+// Plan "pair": up to `parts` workgroups share a row.  Each streams one range
+// of the row's blocks (a fixed number of 32-block key lines) into LDS,
+// publishes its keys in the workspace and counts itself in on the row's
+// counter; the last to arrive gathers the other ranges and selects the row.  Nobody waits, so
 // any residency works.  The gather reads the other workgroups' keys through
 // the L2 of its XCD: the hardware deals workgroups to the 8 XCDs round-robin,
 // so workgroup i runs on XCD i mod 8 and the grid puts a row's parts on one
@@ -995,8 +995,13 @@ __global__ void __launch_bounds__(1024) select_pair_rows_kernel(Params p) {
   uint32_t* area = ctl + kCtlWords;
   uint64_t* s_old = reinterpret_cast<uint64_t*>(ctl + kCtlArrival);
   const RowGeom g = row_geom(p, r, true);
+  // parts of a fixed size (the widest row's share, whole 32-key lines), so
+  // that every busy workgroup streams about the same bytes; a shorter row
+  // uses fewer of its parts and the others leave at once
+  const int32_t cb = (((p.nblocks + H - 1) / H) + 31) & ~31;
+  const int HP = g.nvb > 0 ? (g.nvb + cb - 1) / cb : 1;
+  if (part >= HP) return;
   select_row_prepare(ctl, area, tid, nt);
-  const int32_t cb = (((g.nvb + H - 1) / H) + 31) & ~31;
   const int32_t b0 = part * cb < g.nvb ? part * cb : g.nvb;
   const int32_t b1 = b0 + cb < g.nvb ? b0 + cb : g.nvb;
   stream_blocks<G, kUnroll, true>(p, g, b0, b1, wave, nw, EmitKey{smem});
@@ -1014,9 +1019,9 @@ __global__ void __launch_bounds__(1024) select_pair_rows_kernel(Params p) {
   int arrived = 0;
 #pragma unroll
   for (int x = 0; x < 8; ++x) arrived += (int)((old >> (8 * x)) & 255u);
-  if (arrived != H - 1) return;
+  if (arrived != HP - 1) return;
   if (tid == 0) atomicExch(reinterpret_cast<unsigned long long*>(p.ws_count + r), 0ull);
-  if ((int)((old >> (8 * xcc)) & 255u) == H - 1) {
+  if ((int)((old >> (8 * xcc)) & 255u) == HP - 1) {
     // every other part published its keys in this XCD's L2
     for (int32_t c0 = 0; c0 < g.nvb; c0 += 4 * nt) {
       uint32_t v[4];
@@ -1413,14 +1418,15 @@ int32_t auto_chunk_blocks(int64_t rows, int64_t width, int32_t B) {
 }
 
 // Pair plan shape for `rows` rows of `width` columns: workgroups per row
-// (fill the 256 CUs about once, at most 8) and waves per workgroup (16 once
-// each part is long: from 32K columns a part for 4 and 8 parts, from 128K for
-// 2 parts; measured on decode shapes of 8-128 rows and 32K-256K columns).
+// (fill the 256 CUs about once, at most 8, and parts of at least 8K
+// columns) and waves per workgroup (16 for rows of 256K columns and more;
+// measured on decode shapes of 8-128 rows and 32K-256K columns).
 void pair_shape(int64_t rows, int64_t width, int* parts, int* waves) {
   const int64_t r8 = cdiv(rows, 8) * 8;
-  *parts = r8 <= 32 ? 8 : (r8 <= 64 ? 4 : 2);
-  const int64_t long_part = *parts == 2 ? 262144 : 32768 * (int64_t)*parts;
-  *waves = width >= long_part ? 16 : 8;
+  int64_t n = r8 <= 32 ? 8 : (r8 <= 64 ? 4 : 2);
+  const int64_t by_width = width / 8192 > 2 ? width / 8192 : 2;
+  *parts = (int)(n < by_width ? n : by_width);
+  *waves = width >= 262144 ? 16 : 8;
 }
 
 }  // namespace

@@ -70,7 +70,9 @@ def test_auto_plan():
     # plan_arg = waves | parts << 8
     assert B.select_plan(64, 32768, 64, 32) == (4, 8 | 4 << 8)
     assert B.select_plan(64, 65536, 64, 32) == (4, 8 | 4 << 8)
-    assert B.select_plan(64, 131072, 64, 32) == (4, 16 | 4 << 8)
+    assert B.select_plan(64, 131072, 64, 32) == (4, 8 | 4 << 8)
+    assert B.select_plan(32, 32768, 64, 32) == (4, 8 | 4 << 8)    # parts of >= 8K columns
+    assert B.select_plan(32, 65536, 64, 32) == (4, 8 | 8 << 8)
     assert B.select_plan(128, 131072, 128, 16) == (4, 8 | 2 << 8)
     assert B.select_plan(96, 262144, 128, 16) == (4, 16 | 2 << 8)
     assert B.select_plan(16, 131072, 128, 16) == (4, 8 | 8 << 8)
