@@ -326,6 +326,30 @@ def test_repeat_calls_bit_identical():
     assert np.array_equal(first, exp_out)
 
 
+def test_pair_plan_leaves_counters_zero():
+    """The pair plan's per-row arrival counters (the workspace's first 2048
+    bytes) are zero after every completed call, whatever the part count,
+    the XCD dealing (spread) or the row lengths, so the next call starts
+    clean; results stay identical over repeated calls."""
+    rng = np.random.default_rng(11)
+    for rows, width, B, k in ((64, 32768, 64, 32), (128, 40000, 128, 16), (256, 5000, 8, 40),
+                              (5, 70000, 64, 3)):
+        x = rng.standard_normal((rows, width)).astype(np.float32)
+        ke = rng.integers(-3, width + 3, size=rows).astype(np.int32)
+        w = workloads.Workload(f"pair-{rows}x{width}", x, None, ke, B, k, 1)
+        exp_out, _ = oracle_select(w)
+        xd, ked = dev_logits(x), dev_i32(ke)
+        ws = dsa.Workspace(DEV, dsa.select_workspace_bytes(rows, width, B, k))
+        for arg in (0, 8 | 2 << 8, 4 | 8 << 8, 16 | 3 << 8 | 1 << 16, 1 | 32 << 8):
+            for _ in range(3):
+                out = torch.full((rows, k), 7, dtype=torch.int32, device=DEV)
+                dsa.select_candidate_blocks(xd, None, ked, k, B, out, 1, workspace=ws, plan=4,
+                                            plan_arg=arg)
+                torch.cuda.synchronize()
+                assert np.array_equal(out.cpu().numpy(), exp_out), (w.name, hex(arg))
+                assert int(ws.buf[:2048].count_nonzero()) == 0, (w.name, hex(arg))
+
+
 def test_two_streams_two_workspaces():
     wa, wb = workloads.config(2), workloads.config(4)
     exp_a, _ = oracle_select(wa)
