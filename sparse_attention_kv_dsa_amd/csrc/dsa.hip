@@ -719,12 +719,18 @@ __device__ __forceinline__ uint32_t row_sum16(uint32_t v) {
   return v;
 }
 
-// The general path of select_row (nsel > 64).  RADIX: the candidate bound
-// comes from bound_radix; otherwise from 64 group maxima, group l holding
-// the keys i with i mod 64 == l: T0 = the keff-th largest group maximum.
-// Same-address LDS max serialises per lane on this chip, so the maxima and
-// the bound go through per-wave LDS rows and slots, not atomics.
-template <bool WG, bool RADIX, bool KC>
+// Candidate bounds of select_row_general.
+constexpr int kBoundGroups64 = 0;   // k <= 32
+constexpr int kBoundRadix = 1;      // k > 64
+constexpr int kBoundGroups128 = 2;  // 32 < k <= 64
+
+// The general path of select_row (nsel > 64).  The candidate bound T0 comes
+// from NG group maxima (NG = 64 or 128), group l holding the keys i with
+// i mod NG == l: T0 = the keff-th largest group maximum (keff <= NG), or
+// from bound_radix for larger k.  Same-address LDS max serialises per lane
+// on this chip, so the maxima and the bound go through per-wave LDS rows
+// and slots, not atomics.
+template <bool WG, int BOUND, bool KC>
 __device__ __forceinline__ void select_row_general(const Params& p, const RowGeom& g,
                                                    uint32_t* keys, uint32_t* ctl, uint32_t* area,
                                                    int32_t* out_row, int wave, int nw) {
@@ -736,10 +742,56 @@ __device__ __forceinline__ void select_row_general(const Params& p, const RowGeo
   uint32_t t0, nvalid;
   const LaneKeys lk = lane_keys<KC>(keys, g, wave, nt);
 
-  if constexpr (RADIX) {
+  if constexpr (BOUND == kBoundRadix) {
     bound_radix<WG>(g, k, keys, lk, ctl, area, wave, nw);
     t0 = ctl[kCtlT0];
     nvalid = ctl[kCtlValid];
+  } else if constexpr (BOUND == kBoundGroups128) {
+    // (A) key i belongs to group (i & 63) + 64 * ((i >> 6) & 1).  A lane's
+    // keys i = wave*64 + j*nt + lane fall in half (wave + j*nw) & 1: with an
+    // even wave count always the wave's parity (one maxima row per wave),
+    // with an odd one (nw <= 8) alternately (two rows per wave).
+    uint32_t m0 = 0u, m1 = 0u, nv = 0u;
+    for_lane_keys(lk, keys, g, wave, nt, [&](int32_t i, uint32_t rk) {
+      if ((i >> 6) & 1) m1 = umax(m1, rk);
+      else m0 = umax(m0, rk);
+      nv += (uint32_t)__popcll(__ballot(rk != 0u));
+    });
+    const bool two_rows = (nw & 1) != 0;
+    if (two_rows) {
+      area[(2 * wave) * 64 + lane] = m0;
+      area[(2 * wave + 1) * 64 + lane] = m1;
+    } else {
+      area[wave * 64 + lane] = umax(m0, m1);
+    }
+    if (lane == 0) ctl[kCtlSlotCount + wave] = nv;
+    row_barrier<WG>();
+    // (C) every wave: the 128 group maxima (g0: groups 0-63, g1: 64-127),
+    // then T0 bit by bit from the top: the largest value with at least keff
+    // maxima at or above it is the keff-th largest maximum.
+    uint32_t g0 = 0u, g1 = 0u;
+    for (int w = 0; w < nw; ++w) {
+      if (two_rows) {
+        g0 = umax(g0, area[(2 * w) * 64 + lane]);
+        g1 = umax(g1, area[(2 * w + 1) * 64 + lane]);
+      } else if (w & 1) {
+        g1 = umax(g1, area[w * 64 + lane]);
+      } else {
+        g0 = umax(g0, area[w * 64 + lane]);
+      }
+    }
+    nvalid = (uint32_t)__builtin_amdgcn_readlane(
+        (int)row_sum16(lane < nw ? ctl[kCtlSlotCount + lane] : 0u), 0);
+    const uint32_t kq = (uint32_t)k < nvalid ? (uint32_t)k : nvalid;
+    uint32_t t = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = t | (1u << bit);
+      const uint32_t cnt =
+          (uint32_t)__popcll(__ballot(g0 >= c)) + (uint32_t)__popcll(__ballot(g1 >= c));
+      if (cnt >= kq) t = c;
+    }
+    t0 = t;
+    row_barrier<WG>();  // the maxima rows are read before candidates overwrite them
   } else {
     // (A) per lane: maximum of its keys (all in group `lane`), into this
     // wave's row of `area`; per wave: its count of nonzero keys.
@@ -868,8 +920,12 @@ __device__ __forceinline__ void select_row(const Params& p, int64_t r, const Row
     }
     return;
   }
-  if (k <= 32) select_row_general<WG, false, KC>(p, g, keys, ctl, area, out_row, wave, nw);
-  else select_row_general<WG, true, KC>(p, g, keys, ctl, area, out_row, wave, nw);
+  if (k <= 32)
+    select_row_general<WG, kBoundGroups64, KC>(p, g, keys, ctl, area, out_row, wave, nw);
+  else if (k <= 64 && ((nw & 1) == 0 || nw <= 8))
+    select_row_general<WG, kBoundGroups128, KC>(p, g, keys, ctl, area, out_row, wave, nw);
+  else
+    select_row_general<WG, kBoundRadix, KC>(p, g, keys, ctl, area, out_row, wave, nw);
 }
 
 // Plan "wave": one wave per row, blockDim/64 rows per workgroup, no barrier.
