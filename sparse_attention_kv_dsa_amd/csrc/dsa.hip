@@ -23,8 +23,9 @@
 //   * Scores are kept as order-preserving uint32 keys (unsigned order ==
 //     float order, canonical NaN on top), in LDS for the select.
 //   * Top-k prunes, then ranks: a lower bound on the k-th largest key (the
-//     k-th largest of 64 group maxima for k <= 32, radix passes over 8-bit
-//     digits above), then the keys at or above it (the candidates) are
+//     k-th largest of 64 group maxima for k <= 32, of 128 for k <= 64, radix
+//     passes over 8-bit digits above), then the keys at or above it (the
+//     candidates) are
 //     compacted into LDS as distinct 64-bit words (key, inverted block id),
 //     and a candidate's output slot is the number of larger words.  Every
 //     wave of a row's workgroup takes part; rows with more candidates than
@@ -351,8 +352,9 @@ struct EmitScore {
 //      each group takes its maximum;
 //  (C) T0 = the keff-th largest group maximum, keff = min(k, #nonzero keys).
 //      keff groups each hold a key >= T0, so T0 is a lower bound on the
-//      keff-th largest key: every selected key is >= T0.  For k > 32 the
-//      bound comes from radix passes instead (bound_radix);
+//      keff-th largest key: every selected key is >= T0.  For 32 < k <= 64
+//      the same holds with 128 groups; for larger k the bound comes from
+//      radix passes instead (bound_radix);
 //  (E) the keys >= T0 (the candidates, few for any spread of values) are
 //      compacted into LDS as 64-bit words (rank key << 32 | ~block id), which
 //      are distinct and order exactly as the selection order (key descending,
@@ -1744,12 +1746,12 @@ dsa_status_t dsa_select_from_scores(const float* scores, int64_t rows, int64_t n
   p.wave_words = (int32_t)ww;
   p.out = out;
   p.ld_out = ld_out;
-  // Few rows: a wide workgroup per row (latency); more rows: narrower
+  // Few rows: a wider workgroup per row (latency); more rows: narrower
   // workgroups, so that several rows' selects share each CU (throughput).
-  // Measured on 1024 scores with k = 64: 16 waves are best up to 256 rows,
-  // 4 waves at 512-1024 rows, 2 waves from 2048 rows on.
+  // Measured on 1024 scores with k = 64: 4 waves are best up to 512 rows,
+  // 2 waves from 1024 rows on (8 and 16 waves were slower everywhere).
   int64_t waves = cdiv(nblocks, 64);
-  const int64_t cap = rows <= 256 ? 16 : (rows <= 1024 ? kWaves : 2);
+  const int64_t cap = rows <= 512 ? kWaves : 2;
   if (waves > cap) waves = cap;
   return launch(reinterpret_cast<void*>(&select_scores_kernel), rows, 64 * (int)waves, 1,
                 (size_t)ww * 4, stream, p);
