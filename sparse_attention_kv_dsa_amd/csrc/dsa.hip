@@ -768,32 +768,37 @@ __device__ __forceinline__ void select_row_general(const Params& p, const RowGeo
     }
     if (lane == 0) ctl[kCtlSlotCount + wave] = nv;
     row_barrier<WG>();
-    // (C) every wave: the 128 group maxima (g0: groups 0-63, g1: 64-127),
-    // then T0 bit by bit from the top: the largest value with at least keff
-    // maxima at or above it is the keff-th largest maximum.
-    uint32_t g0 = 0u, g1 = 0u;
-    for (int w = 0; w < nw; ++w) {
-      if (two_rows) {
-        g0 = umax(g0, area[(2 * w) * 64 + lane]);
-        g1 = umax(g1, area[(2 * w + 1) * 64 + lane]);
-      } else if (w & 1) {
-        g1 = umax(g1, area[w * 64 + lane]);
-      } else {
-        g0 = umax(g0, area[w * 64 + lane]);
-      }
-    }
+    // (C) wave 0: the 128 group maxima (g0: groups 0-63, g1: 64-127), then
+    // T0 bit by bit from the top: the largest value with at least keff
+    // maxima at or above it is the keff-th largest maximum.  One wave does
+    // it (the others wait at the barrier anyway): where many rows share a
+    // CU, its compares are VALU time the other waves would also spend.
     nvalid = (uint32_t)__builtin_amdgcn_readlane(
         (int)row_sum16(lane < nw ? ctl[kCtlSlotCount + lane] : 0u), 0);
-    const uint32_t kq = (uint32_t)k < nvalid ? (uint32_t)k : nvalid;
-    uint32_t t = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t c = t | (1u << bit);
-      const uint32_t cnt =
-          (uint32_t)__popcll(__ballot(g0 >= c)) + (uint32_t)__popcll(__ballot(g1 >= c));
-      if (cnt >= kq) t = c;
+    if (wave == 0) {
+      uint32_t g0 = 0u, g1 = 0u;
+      for (int w = 0; w < nw; ++w) {
+        if (two_rows) {
+          g0 = umax(g0, area[(2 * w) * 64 + lane]);
+          g1 = umax(g1, area[(2 * w + 1) * 64 + lane]);
+        } else if (w & 1) {
+          g1 = umax(g1, area[w * 64 + lane]);
+        } else {
+          g0 = umax(g0, area[w * 64 + lane]);
+        }
+      }
+      const uint32_t kq = (uint32_t)k < nvalid ? (uint32_t)k : nvalid;
+      uint32_t t = 0u;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = t | (1u << bit);
+        const uint32_t cnt =
+            (uint32_t)__popcll(__ballot(g0 >= c)) + (uint32_t)__popcll(__ballot(g1 >= c));
+        if (cnt >= kq) t = c;
+      }
+      if (lane == 0) ctl[kCtlT0] = t;
     }
-    t0 = t;
-    row_barrier<WG>();  // the maxima rows are read before candidates overwrite them
+    row_barrier<WG>();  // T0 is out, and the maxima rows are read before candidates overwrite them
+    t0 = ctl[kCtlT0];
   } else {
     // (A) per lane: maximum of its keys (all in group `lane`), into this
     // wave's row of `area`; per wave: its count of nonzero keys.
