@@ -153,17 +153,21 @@ dsa_status_t dsa_select_candidate_blocks(const float* logits, int64_t rows, int6
  *                 4: pair: several workgroups share a row, each streaming a
  *                    range of its blocks and publishing its keys in the
  *                    workspace; the last to arrive (per-row atomic counter)
- *                    gathers the rest and selects.  A row's workgroups are
- *                    dealt to one XCD so that the keys pass through its L2;
- *                    a part that ran on another XCD is streamed again by the
- *                    selecting workgroup.  At most 256 rows.
+ *                    gathers the rest and selects.  The ranges have a fixed
+ *                    size, ceil(nblocks / parts) rounded up to 32 blocks, so
+ *                    a shorter row uses fewer of its workgroups.  A row's
+ *                    workgroups are dealt to one XCD so that the keys pass
+ *                    through its L2; a part that ran on another XCD is
+ *                    streamed again by the selecting workgroup.  At most
+ *                    256 rows.
  *   plan_arg      plan 1: waves per workgroup, 1..16 (0: 4);
  *                 plan 2: blocks per chunk, >= 1 (0: automatic);
  *                 plan 3: float4 loads in flight per lane, 8 or 16 (0: 8);
  *                 plan 4: waves | parts << 8 | spread << 16: waves per
  *                    workgroup 0..16 and workgroups per row 0..255 (0:
- *                    automatic), spread 1 deals a row's workgroups to
- *                    different XCDs (for tests of the fallback).
+ *                    automatic; 1 selects each row in one workgroup);
+ *                    spread 1 deals a row's workgroups to different XCDs
+ *                    (for tests of the fallback).
  */
 dsa_status_t dsa_select_candidate_blocks_plan(
     const float* logits, int64_t rows, int64_t width, int64_t ld_logits,
