@@ -1068,40 +1068,42 @@ __global__ void __launch_bounds__(1024) select_pair_rows_kernel(Params p) {
   const int32_t b0 = part * cb < g.nvb ? part * cb : g.nvb;
   const int32_t b1 = b0 + cb < g.nvb ? b0 + cb : g.nvb;
   stream_blocks<G, kUnroll, true>(p, g, b0, b1, wave, nw, EmitKey{smem});
-  __syncthreads();
-  uint32_t* wrow = p.ws_keys + r * p.ws_ld;
-  for (int32_t b = b0 + tid; b < b1; b += nt) wrow[b] = smem[b];
-  // every key store acknowledged by L2 before the arrival is counted
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  const uint32_t xcc = xcc_id();
-  if (tid == 0) *s_old = atomicAdd(reinterpret_cast<unsigned long long*>(p.ws_count + r),
-                                  1ull << (8 * xcc));
-  __syncthreads();
-  const uint64_t old = *s_old;
-  int arrived = 0;
+  if (HP > 1) {  // workgroup-uniform; a row of one part needs no hand-off
+    __syncthreads();
+    uint32_t* wrow = p.ws_keys + r * p.ws_ld;
+    for (int32_t b = b0 + tid; b < b1; b += nt) wrow[b] = smem[b];
+    // every key store acknowledged by L2 before the arrival is counted
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const uint32_t xcc = xcc_id();
+    if (tid == 0) *s_old = atomicAdd(reinterpret_cast<unsigned long long*>(p.ws_count + r),
+                                    1ull << (8 * xcc));
+    __syncthreads();
+    const uint64_t old = *s_old;
+    int arrived = 0;
 #pragma unroll
-  for (int x = 0; x < 8; ++x) arrived += (int)((old >> (8 * x)) & 255u);
-  if (arrived != HP - 1) return;
-  if (tid == 0) atomicExch(reinterpret_cast<unsigned long long*>(p.ws_count + r), 0ull);
-  if ((int)((old >> (8 * xcc)) & 255u) == HP - 1) {
-    // every other part published its keys in this XCD's L2
-    for (int32_t c0 = 0; c0 < g.nvb; c0 += 4 * nt) {
-      uint32_t v[4];
+    for (int x = 0; x < 8; ++x) arrived += (int)((old >> (8 * x)) & 255u);
+    if (arrived != HP - 1) return;
+    if (tid == 0) atomicExch(reinterpret_cast<unsigned long long*>(p.ws_count + r), 0ull);
+    if ((int)((old >> (8 * xcc)) & 255u) == HP - 1) {
+      // every other part published its keys in this XCD's L2
+      for (int32_t c0 = 0; c0 < g.nvb; c0 += 4 * nt) {
+        uint32_t v[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int32_t b = c0 + q * nt + tid;
-        v[q] = (b < g.nvb && (b < b0 || b >= b1)) ? wrow[b] : 0u;
+        for (int q = 0; q < 4; ++q) {
+          const int32_t b = c0 + q * nt + tid;
+          v[q] = (b < g.nvb && (b < b0 || b >= b1)) ? wrow[b] : 0u;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int32_t b = c0 + q * nt + tid;
+          if (b < g.nvb && (b < b0 || b >= b1)) smem[b] = v[q];
+        }
       }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int32_t b = c0 + q * nt + tid;
-        if (b < g.nvb && (b < b0 || b >= b1)) smem[b] = v[q];
-      }
+    } else {
+      stream_blocks<G, kUnroll, true>(p, g, 0, b0, wave, nw, EmitKey{smem});
+      stream_blocks<G, kUnroll, true>(p, g, b1, g.nvb, wave, nw, EmitKey{smem});
     }
-  } else {
-    stream_blocks<G, kUnroll, true>(p, g, 0, b0, wave, nw, EmitKey{smem});
-    stream_blocks<G, kUnroll, true>(p, g, b1, g.nvb, wave, nw, EmitKey{smem});
   }
   __syncthreads();
   select_row<true>(p, r, g, smem, ctl, area, wave, nw);
