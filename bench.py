@@ -247,7 +247,30 @@ def _time_steps(launch, K, W, copies, dev, use_graph):
             launch(i % copies)
     e1.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / K
+    first = e0.elapsed_time(e1) / K
+    # the reported step time is the region above; four more replays of the
+    # same K steps give its spread
+    _REPEATS[:] = [first]
+    if use_graph:
+        for _ in range(4):
+            e0.record(stream)
+            graphs["timed"].replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            _REPEATS.append(e0.elapsed_time(e1) / K)
+    return first
+
+
+_REPEATS: list = []
+
+
+def _repeats_field():
+    """min / median / max ms per step over the timed region and its repeats."""
+    v = sorted(_REPEATS)
+    if not v:
+        return None
+    return {"n": len(v), "ms_per_step_min": round(v[0], 6),
+            "ms_per_step_median": round(v[len(v) // 2], 6), "ms_per_step_max": round(v[-1], 6)}
 
 
 def bench_next(args):
@@ -412,6 +435,7 @@ def bench_next(args):
            "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms, 6),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
            "data": "synthetic", "config": dict(cfg, graph=use_graph), "parity": parity,
+           "repeats": _repeats_field(),
            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                         "traffic": traffic_for(cfg["workload"], 0),
@@ -535,6 +559,16 @@ def main():
     ms = e0.elapsed_time(e1) / K
     print(f"# timed {K} steps: {ms * 1e3:.2f} us/step (wall {wall:.3f} s)", file=sys.stderr,
           flush=True)
+    # the reported step time is the region above; four more replays of the
+    # same K steps give its spread
+    _REPEATS[:] = [ms]
+    if use_graph:
+        for _ in range(4):
+            e0.record(stream)
+            graphs["timed"].replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            _REPEATS.append(e0.elapsed_time(e1) / K)
     # every launch of the timed region wrote the same ids
     assert np.array_equal(out.cpu().numpy(), got), "timed launches disagree with the checked one"
 
@@ -553,6 +587,7 @@ def main():
                    "logits_sha256": workloads.sha256(w.logits)[:16]},
         "rows_per_s": round(w.rows / (ms * 1e-3), 1),
         "parity": parity,
+        "repeats": _repeats_field(),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_for(w.name, plan),
