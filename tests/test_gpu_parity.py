@@ -388,6 +388,24 @@ def test_large_k_and_full_sort():
             assert_same(got, sc, exp_out, exp_sc, f"k={k} plan {plan}")
 
 
+def test_bounds_by_wave_count_and_k():
+    """The candidate bound of the workgroup select for every wave-count
+    parity: 64 group maxima (k <= 32), 128 (32 < k <= 64; one maxima row per
+    wave for even counts, two for odd counts up to 8) and the radix passes
+    (k > 64, and odd counts above 8 with 32 < k <= 64)."""
+    rng = np.random.default_rng(17)
+    x = np.round(rng.standard_normal((6, 40000)).astype(np.float32) * 8) / 8
+    x[0] = np.abs(x[0]) + 2.0          # same sign and exponent range: clustered keys
+    x[1, ::5] = -np.inf
+    ke = np.array([40000, 39000, 30000, 20000, 9000, 4500], np.int32)
+    for k in (31, 33, 64, 65, 100):
+        w = workloads.Workload(f"bounds-k{k}", x, None, ke, 32, k, 1)
+        exp_out, exp_sc = oracle_select(w)
+        for waves in (1, 2, 3, 5, 7, 8, 9, 12, 15, 16):
+            got, sc = gpu_select(w, 1, waves)
+            assert_same(got, sc, exp_out, exp_sc, f"k={k} waves={waves}")
+
+
 def test_all_equal_scores_take_lowest_ids():
     x = np.full((3, 4096), 1.5, np.float32)
     ke = np.array([4096, 100, 4095], np.int32)
