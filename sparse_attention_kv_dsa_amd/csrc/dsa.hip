@@ -223,8 +223,9 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 // load for the next round is issued as soon as tile j has been reduced, so U
 // loads stay in flight across rounds instead of draining at each round's end
 // (emits into HBM would count against the same in-order load counter, so
-// those callers take whole rounds).
-template <int G, int U, bool ROLL, class Emit>
+// those callers take whole rounds).  FULL: a tile wholly inside the window
+// (a wave-uniform test) skips the per-unit masks.
+template <int G, int U, bool ROLL, bool FULL, class Emit>
 __device__ __forceinline__ void stream_vec(const RowGeom& g, int32_t b0, int32_t b1, int wv,
                                            int nw, const Emit& emit) {
   const int lane = threadIdx.x & 63;
@@ -242,14 +243,21 @@ __device__ __forceinline__ void stream_vec(const RowGeom& g, int32_t b0, int32_t
     const uint32_t off = (uint32_t)(u < ue ? u : ue - 1) << 4;
     return load_stream(static_cast<const void*>(cbase + off));
   };
+  // units [0, full) hold only in-window columns
+  const int32_t full = ue < (span >> 2) ? ue : (span >> 2);
   auto reduce = [&](int32_t t, const float4& x4) {
     const int32_t u = ub + (t << 6) + lane;
-    const int32_t lim = u < ue ? span - 4 * u : 0;  // valid columns in this unit
-    const float x = lim > 0 ? x4.x : ninf;
-    const float y = lim > 1 ? x4.y : ninf;
-    const float z = lim > 2 ? x4.z : ninf;
-    const float w = lim > 3 ? x4.w : ninf;
-    float m = fmaximum(fmaximum(x, y), fmaximum(z, w));
+    float m;
+    if (FULL && ub + (t << 6) + 64 <= full) {  // wave-uniform: the tile is all in the window
+      m = fmaximum(fmaximum(x4.x, x4.y), fmaximum(x4.z, x4.w));
+    } else {
+      const int32_t lim = u < ue ? span - 4 * u : 0;  // valid columns in this unit
+      const float x = lim > 0 ? x4.x : ninf;
+      const float y = lim > 1 ? x4.y : ninf;
+      const float z = lim > 2 ? x4.z : ninf;
+      const float w = lim > 3 ? x4.w : ninf;
+      m = fmaximum(fmaximum(x, y), fmaximum(z, w));
+    }
     m = group_max<G>(m);
     if (t < ntiles) {
       const int32_t b = b0 + (((t << 6) + lane) / G);
@@ -318,13 +326,13 @@ __device__ __forceinline__ void stream_scalar(const RowGeom& g, int32_t B, int32
   }
 }
 
-template <int G, int U, bool ROLL, class Emit>
+template <int G, int U, bool ROLL, bool FULL = false, class Emit>
 __device__ __forceinline__ void stream_blocks(const Params& p, const RowGeom& g, int32_t b0,
                                               int32_t b1, int wv, int nw, const Emit& emit) {
   if (b1 <= b0) return;
   if constexpr (G > 0) {
     if (p.vec_ok && g.s >= 0 && ((reinterpret_cast<uintptr_t>(g.row + g.s) & 15u) == 0)) {
-      stream_vec<G, U, ROLL>(g, b0, b1, wv, nw, emit);
+      stream_vec<G, U, ROLL, FULL>(g, b0, b1, wv, nw, emit);
       return;
     }
   }
@@ -948,7 +956,7 @@ __global__ void __launch_bounds__(kThreads) select_wave_rows_kernel(Params p) {
   for (int64_t r = (int64_t)blockIdx.x * nw + wave; r < p.items; r += (int64_t)gridDim.x * nw) {
     const RowGeom g = row_geom(p, r, true);
     select_row_prepare(ctl, area, threadIdx.x & 63, 64);
-    stream_blocks<G, U, true>(p, g, 0, g.nvb, 0, 1, EmitKey{keys});
+    stream_blocks<G, U, true, true>(p, g, 0, g.nvb, 0, 1, EmitKey{keys});
     wave_sync();
     select_row<false>(p, r, g, keys, ctl, area, 0, 1);
     wave_sync();
@@ -967,7 +975,7 @@ __global__ void __launch_bounds__(1024) select_group_rows_kernel(Params p) {
   for (int64_t r = blockIdx.x; r < p.items; r += gridDim.x) {
     const RowGeom g = row_geom(p, r, true);
     select_row_prepare(ctl, area, threadIdx.x, blockDim.x);
-    stream_blocks<G, kUnroll, true>(p, g, 0, g.nvb, wave, nw, EmitKey{smem});
+    stream_blocks<G, kUnroll, true, true>(p, g, 0, g.nvb, wave, nw, EmitKey{smem});
     __syncthreads();
     select_row<true>(p, r, g, smem, ctl, area, wave, nw);
     if (r + gridDim.x < p.items) __syncthreads();  // LDS is reused by the next row
@@ -1042,7 +1050,9 @@ __device__ __forceinline__ uint32_t xcc_id() {
   return (uint32_t)__builtin_amdgcn_s_getreg(20 | (0 << 6) | (15 << 11)) & 7u;
 }
 
-template <int G>
+// FULL (chosen on the host): parts of 8 tiles or more per wave skip the
+// masks on interior tiles; short parts measured faster without that test.
+template <int G, bool FULL>
 __global__ void __launch_bounds__(1024) select_pair_rows_kernel(Params p) {
   extern __shared__ uint32_t smem[];
   const int wave = wave_index();
@@ -1067,7 +1077,7 @@ __global__ void __launch_bounds__(1024) select_pair_rows_kernel(Params p) {
   select_row_prepare(ctl, area, tid, nt);
   const int32_t b0 = part * cb < g.nvb ? part * cb : g.nvb;
   const int32_t b1 = b0 + cb < g.nvb ? b0 + cb : g.nvb;
-  stream_blocks<G, kUnroll, true>(p, g, b0, b1, wave, nw, EmitKey{smem});
+  stream_blocks<G, kUnroll, true, FULL>(p, g, b0, b1, wave, nw, EmitKey{smem});
   if (HP > 1) {  // workgroup-uniform; a row of one part needs no hand-off
     __syncthreads();
     uint32_t* wrow = p.ws_keys + r * p.ws_ld;
@@ -1101,8 +1111,8 @@ __global__ void __launch_bounds__(1024) select_pair_rows_kernel(Params p) {
         }
       }
     } else {
-      stream_blocks<G, kUnroll, true>(p, g, 0, b0, wave, nw, EmitKey{smem});
-      stream_blocks<G, kUnroll, true>(p, g, b1, g.nvb, wave, nw, EmitKey{smem});
+      stream_blocks<G, kUnroll, true, FULL>(p, g, 0, b0, wave, nw, EmitKey{smem});
+      stream_blocks<G, kUnroll, true, FULL>(p, g, b1, g.nvb, wave, nw, EmitKey{smem});
     }
   }
   __syncthreads();
@@ -1412,7 +1422,22 @@ DSA_WAVE_TABLE(8)
 DSA_WAVE_TABLE(16)
 DSA_KERNEL_TABLE(select_group_rows_kernel)
 DSA_KERNEL_TABLE(stream_keys_kernel)
-DSA_KERNEL_TABLE(select_pair_rows_kernel)
+
+#define DSA_PAIR_TABLE(NAME, FULL)                                                    \
+  void* NAME(int g) {                                                                 \
+    switch (g) {                                                                      \
+      case 1: return reinterpret_cast<void*>(&select_pair_rows_kernel<1, FULL>);      \
+      case 2: return reinterpret_cast<void*>(&select_pair_rows_kernel<2, FULL>);      \
+      case 4: return reinterpret_cast<void*>(&select_pair_rows_kernel<4, FULL>);      \
+      case 8: return reinterpret_cast<void*>(&select_pair_rows_kernel<8, FULL>);      \
+      case 16: return reinterpret_cast<void*>(&select_pair_rows_kernel<16, FULL>);    \
+      case 32: return reinterpret_cast<void*>(&select_pair_rows_kernel<32, FULL>);    \
+      case 64: return reinterpret_cast<void*>(&select_pair_rows_kernel<64, FULL>);    \
+      default: return reinterpret_cast<void*>(&select_pair_rows_kernel<0, FULL>);     \
+    }                                                                                 \
+  }
+DSA_PAIR_TABLE(select_pair_rows_ptr, false)
+DSA_PAIR_TABLE(select_pair_rows_full_ptr, true)
 DSA_KERNEL_TABLE(block_scores_kernel)
 
 // Launches `fn` over `items` work items with `threads` per workgroup and
@@ -1693,7 +1718,11 @@ dsa_status_t dsa_select_candidate_blocks_plan(
     if (plan_arg & 255) waves = plan_arg & 255;
     p.parts = parts;
     p.spread = plan_arg >> 16;
-    return launch(select_pair_rows_kernel_ptr(g), 8 * parts * cdiv(rows, 8), 64 * waves, 1,
+    // parts of 8 wave tiles or more per wave take the unmasked interior path
+    const int64_t part_units = ((cdiv(nblocks, parts) + 31) / 32) * 32 * g;
+    void* fn = part_units >= 64 * 8 * (int64_t)waves ? select_pair_rows_full_ptr(g)
+                                                      : select_pair_rows_ptr(g);
+    return launch(fn, 8 * parts * cdiv(rows, 8), 64 * waves, 1,
                   (size_t)ww * 4, stream, p);
   }
   p.chunk_blocks = plan_arg < p.nblocks ? plan_arg : p.nblocks;
