@@ -1219,14 +1219,22 @@ __global__ void __launch_bounds__(kThreads) mask_candidates_kernel(MaskParams m)
   const int nt = blockDim.x;
   const float ninf = -__builtin_inff();
   for (int64_t item = blockIdx.x; item < m.items; item += gridDim.x) {
-    const int64_t r = item / m.nchunks;
+    // 32-bit divides when they fit (they precede every load of the item)
+    const int64_t r = ((item | m.nchunks) >> 32) == 0
+                          ? (int64_t)((uint32_t)item / (uint32_t)m.nchunks)
+                          : item / m.nchunks;
     const int64_t c0 = (item - r * m.nchunks) * kMaskChunk;
     const int64_t c1 = c0 + kMaskChunk < m.width ? c0 + kMaskChunk : m.width;
-    const int64_t grp = r / m.R;
+    const int64_t grp = m.R == 1 ? r : ((r >> 32) == 0 ? (int64_t)((uint32_t)r / (uint32_t)m.R)
+                                                       : r / m.R);
     const int32_t* cr = m.k > 0 ? m.cand + r * m.ld_cand : m.cand;
     const int32_t cid = tid < m.k ? cr[tid] : -1;  // issued before the bounds are known
-    const int64_t s = m.ks ? (int64_t)m.ks[grp] : 0;
-    const int64_t e = (int64_t)m.ke[grp];
+    // one load brings both bounds (lane 0 of each wave: the start, the
+    // others: the end); every lane of the workgroup is active here
+    const int32_t* bp = ((tid & 63) == 0 && m.ks) ? m.ks + grp : m.ke + grp;
+    const int32_t bv = *bp;
+    const int64_t s = m.ks ? (int64_t)__builtin_amdgcn_readlane(bv, 0) : 0;
+    const int64_t e = (int64_t)__builtin_amdgcn_readlane(bv, 1);
     const int64_t lo = c0 > s ? c0 : s;  // in-window columns of this chunk: [lo, hi)
     const int64_t hi = c1 < e ? c1 : e;
     int64_t blo = 0, nb = 0;             // their blocks: [blo, blo + nb)
