@@ -60,10 +60,12 @@ def parse():
                     help="short eager run for rocprofv3: no graph, no oracle timing, no context runs")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain copy of this many MiB (counter scale for rocprofv3 --pmc)")
-    ap.add_argument("--op", default="select", choices=["select", "scores", "mask", "lse"],
+    ap.add_argument("--op", default="select",
+                    choices=["select", "scores", "mask", "lse", "blockscores"],
                     help="select: candidate-block selection (the headline, default); scores: the "
                          "DCP selection from reduced scores; mask: candidate masking; lse: the "
-                         "base-2 LSE correction")
+                         "base-2 LSE correction; blockscores: one DCP rank's local block "
+                         "scores (pin off)")
     return ap.parse_args()
 
 
@@ -383,6 +385,49 @@ def bench_next(args):
             return {"value": round(written * sub / w.rows / per / 1e9, 4), "unit": "GB/s", "cores": 1,
                     "kind": "oracle",
                     "sample": f"the first {sub} rows of the prefill chunk, {reps} calls in {el:.1f} s, one thread"}
+    elif args.op == "blockscores":
+        import oracle
+        w = workloads.dcp_local_logits()
+        nb = -(-w.width // w.block_size)
+        copies = 1 if args.profile else max(1, min(512, int(-(-args.rotate_bytes * 2**30 // w.logits.nbytes))))
+        xs = [torch.from_numpy(w.logits).to(dev) for _ in range(copies)]
+        ks, ke = i32(w.row_ks), i32(w.row_ke)
+        sc = torch.empty((w.rows, nb), dtype=torch.float32, device=dev)
+        dsa.block_scores(xs[0], ks, ke, w.block_size, 1, pin_newest=False, out=sc)
+        torch.cuda.synchronize()
+        srows = np.linspace(0, w.rows - 1, 64).astype(np.int64)
+        exp = oracle.block_scores(np.ascontiguousarray(w.logits[srows]), w.row_ks[srows],
+                                  w.row_ke[srows], w.block_size, 1, pin_newest=False)
+        parity = bool(np.array_equal(sc.cpu().numpy()[srows].view(np.uint32), exp.view(np.uint32)))
+
+        def launch(i):
+            dsa.block_scores(xs[i], ks, ke, w.block_size, 1, pin_newest=False, out=sc)
+
+        read = in_window_bytes(w)
+        written = w.rows * nb * 4
+        alg = read + written + w.rows * 8
+        metric = "DCP local block scores: logits GB/s (fraction of HBM peak), 1 GPU"
+        value_bytes, kernel = read, "block_scores_kernel"
+        cfg = {"workload": w.name, "rows": w.rows, "width": w.width, "block_size": w.block_size,
+               "pin_newest": False, "input_copies": copies, "scores_bytes": written}
+
+        def cpu(budget):
+            sub = 64
+            y = np.ascontiguousarray(w.logits[:sub])
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                oracle.block_scores(y, w.row_ks[:sub], w.row_ke[:sub], w.block_size, 1,
+                                    pin_newest=False)
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= budget:
+                    break
+            per = el / reps
+            sub_read = in_window_bytes(workloads.Workload(w.name, y, w.row_ks[:sub].copy(),
+                                                          w.row_ke[:sub].copy(), w.block_size, 0, 1))
+            return {"value": round(sub_read / per / 1e9, 4), "unit": "GB/s", "cores": 1,
+                    "kind": "oracle",
+                    "sample": f"the first {sub} rows of {w.name}, {reps} calls in {el:.1f} s, one thread"}
     else:
         import oracle
         w = workloads.lse_merge()
@@ -442,7 +487,8 @@ def bench_next(args):
                         "algorithmic_bytes_per_launch": alg, "kernel": kernel}}
     if not args.profile:
         res["context"] = _stream_context(dev, achieved, {"scores": "read", "mask": "fill",
-                                                          "lse": "copy"}[args.op])
+                                                          "lse": "copy",
+                                                          "blockscores": "read"}[args.op])
     if args.cpu_seconds > 0 and not args.profile:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu(args.cpu_seconds)

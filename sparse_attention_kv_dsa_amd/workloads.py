@@ -126,6 +126,35 @@ def large_prefill(rows: int = 8192) -> Workload:
     return Workload(NAMES[5], logits, ks[:rows].copy(), ke[:rows].copy(), 64, 64, 1)
 
 
+def dcp_local_logits(rows: int = 8192, world: int = 8) -> Workload:
+    """Rank 0's share of the large prefill under decode-context parallelism
+    over ``world`` ranks: tokens are dealt t mod world, so the rank holds
+    width 65536 / world local columns and scores blocks of 64 / world of
+    them (pin off; the reduce across ranks and the pin come after).  Values
+    are a fresh draw of the large prefill's distribution at the local shape
+    (uniform(-8, 8) rounded to 1/16, in 512-row chunks, seed 400); the bounds
+    are the large prefill's, mapped to rank 0's columns: start ceil(s / world),
+    end ceil(e / world)."""
+    rng = _rng(400)
+    width, B = 65536 // world, 64 // world
+    logits = np.empty((rows, width), dtype=np.float32)
+    for r0 in range(0, rows, 512):
+        r1 = min(r0 + 512, rows)
+        x = rng.random((r1 - r0, width), dtype=np.float32)
+        x *= np.float32(16.0)
+        x -= np.float32(8.0)
+        x *= np.float32(16.0)
+        np.rint(x, out=x)
+        x /= np.float32(16.0)
+        logits[r0:r1] = x
+    r = np.arange(rows)
+    gs = np.where(r < rows // 2, 0, 32768).astype(np.int64)
+    ge = gs + 28672 + (r % max(rows // 2, 1)) + 1
+    ks = (-(-gs // world)).astype(np.int32)
+    ke = (-(-ge // world)).astype(np.int32)
+    return Workload(f"dcp-local-logits-{rows}x{width}-b{B}", logits, ks, ke, B, 0, 1)
+
+
 def config(i: int) -> Workload:
     return {1: tiny, 2: decode, 3: prefill, 4: longctx_decode, 5: large_prefill}[i]()
 

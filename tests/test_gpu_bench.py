@@ -18,7 +18,7 @@ def _run(*args):
     return json.loads(r.stdout.strip().splitlines()[-1])
 
 
-@pytest.mark.parametrize("args", [("--config", "1"), ("--op", "lse")])
+@pytest.mark.parametrize("args", [("--config", "1"), ("--op", "lse"), ("--op", "blockscores")])
 def test_bench_line(args):
     d = _run(*args, "--steps", "20", "--warmup", "5", "--cpu-seconds", "0.5",
              "--rotate-bytes", "0.25")

@@ -117,6 +117,25 @@ def test_dcp_decomposition_on_gpu(W):
     assert np.array_equal(ref.cpu().numpy(), exp)
 
 
+def test_dcp_local_scores_full_size():
+    """One DCP rank's local block scores (pin off) at the size the bench
+    times: 8192 rows of 8192 local columns, blocks of 8; every score of 128
+    sampled rows bit for bit, and -inf past every row's window."""
+    w = workloads.dcp_local_logits()
+    _say("dcp local scores", w.name)
+    x = torch.from_numpy(w.logits).to(DEV)
+    sc = dsa.block_scores(x, _i32(w.row_ks), _i32(w.row_ke), w.block_size, 1, pin_newest=False)
+    got = sc.cpu().numpy()
+    rows = np.linspace(0, w.rows - 1, 128).astype(np.int64)
+    exp = oracle.block_scores(np.ascontiguousarray(w.logits[rows]), w.row_ks[rows], w.row_ke[rows],
+                              w.block_size, 1, pin_newest=False)
+    assert np.array_equal(got[rows].view(np.uint32), exp.view(np.uint32))
+    nb = got.shape[1]
+    last = -(-(w.row_ke.astype(np.int64) - w.row_ks) // w.block_size)   # blocks with a column
+    col = np.arange(nb)[None, :]
+    assert np.all(np.isneginf(got[col >= last[:, None]]))
+
+
 # ------------------------------------------------------------------- masking
 
 def _dev_rows(x, ld_pad, offset):
