@@ -219,12 +219,12 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 // the block.
 //
 // The loads are branch-free: a lane past the chunk's last unit re-reads that
-// unit (same cache line) and masks it.  ROLL (for emits into LDS): tile j's
-// load for the next round is issued as soon as tile j has been reduced, so U
-// loads stay in flight across rounds instead of draining at each round's end
-// (emits into HBM would count against the same in-order load counter, so
-// those callers take whole rounds).  FULL: a tile wholly inside the window
-// (a wave-uniform test) skips the per-unit masks.
+// unit (same cache line) and masks it.  ROLL: tile j's load for the next
+// round is issued as soon as tile j has been reduced, so U loads stay in
+// flight across rounds instead of draining at each round's end.  Emits into
+// HBM then sit in the same in-order memory counter as the loads; whether
+// rolling still pays is measured per caller.  FULL: a tile wholly inside the
+// window (a wave-uniform test) skips the per-unit masks.
 template <int G, int U, bool ROLL, bool FULL, class Emit>
 __device__ __forceinline__ void stream_vec(const RowGeom& g, int32_t b0, int32_t b1, int wv,
                                            int nw, const Emit& emit) {
@@ -1120,7 +1120,10 @@ __global__ void __launch_bounds__(1024) select_pair_rows_kernel(Params p) {
 }
 
 // Block scores to HBM; item = r * nchunks + c covers blocks
-// [c*chunk_blocks, (c+1)*chunk_blocks) of row r, in-window or not.
+// [c*chunk_blocks, (c+1)*chunk_blocks) of row r, in-window or not.  The
+// loads roll across rounds although the emits are HBM stores: measured on
+// five shapes, the stores' place in the in-order memory counter costs less
+// than the drained rounds did.
 template <int G>
 __global__ void __launch_bounds__(kThreads) block_scores_kernel(Params p) {
   const int wave = wave_index();
@@ -1133,7 +1136,7 @@ __global__ void __launch_bounds__(kThreads) block_scores_kernel(Params p) {
     const int32_t b1 = b0 + p.chunk_blocks < p.nblocks ? b0 + p.chunk_blocks : p.nblocks;
     float* srow = p.scores + r * p.ld_scores;
     const int32_t sb1 = b1 < g.nvb ? b1 : g.nvb;
-    stream_blocks<G, kUnroll, false>(p, g, b0, sb1, wave, nw, EmitScore{srow, g.pin});
+    stream_blocks<G, kUnroll, true, true>(p, g, b0, sb1, wave, nw, EmitScore{srow, g.pin});
     const int32_t f0 = b0 > g.nvb ? b0 : g.nvb;
     for (int32_t b = f0 + (int32_t)threadIdx.x; b < b1; b += (int32_t)blockDim.x)
       srow[b] = b == g.pin ? __builtin_inff() : -__builtin_inff();
@@ -1618,16 +1621,25 @@ dsa_status_t dsa_block_scores(const float* logits, int64_t rows, int64_t width,
   p.pin = pin_newest;
   p.nblocks = (int32_t)nblocks;
   p.vec_ok = (width % 4) == 0 && width < ((int64_t)1 << 30);
-  // ~8K columns per workgroup, a whole number of wave tiles.
-  int64_t cb = cdiv(8192, block_size);
+  // Items are row chunks: 8K columns, doubled until at most 512 items
+  // remain (few rows: chunks spread each row over many CUs), or whole rows
+  // from 1024 rows on.  Whole rows take one wave below 32K columns (short
+  // windows: more rows in flight per CU), else four.  Measured against fixed
+  // 8K chunks of four waves: large prefill 8192x65536 300 -> 172 us, prefill
+  // chunk 4096x16384 32 -> 13.5, 8192x8192 at B = 8 35 -> 30.5, 128x131072
+  // 13.4 -> 11.7; 64x32768 unchanged at 4.5.
   const int g = lanes_per_block(block_size);
+  int64_t ccols = 8192;
+  while (ccols < width && rows * cdiv(width, ccols) > 512) ccols *= 2;
+  int64_t cb = rows >= 1024 ? nblocks : cdiv(ccols, block_size);
   if (g > 0) cb = cdiv(cb, 64 / g) * (64 / g);
   if (cb > nblocks) cb = nblocks;
+  const int threads = rows >= 1024 && width < 32768 ? 64 : kThreads;
   p.chunk_blocks = (int32_t)cb;
   p.nchunks = (int32_t)cdiv(nblocks, cb);
   p.scores = scores;
   p.ld_scores = ld_scores;
-  return launch(block_scores_kernel_ptr(g), rows * p.nchunks, kThreads, 1, 0, stream, p);
+  return launch(block_scores_kernel_ptr(g), rows * p.nchunks, threads, 1, 0, stream, p);
 }
 
 dsa_status_t dsa_select_candidate_blocks_plan(

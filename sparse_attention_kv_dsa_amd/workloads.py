@@ -191,6 +191,24 @@ def random_case(seed: int, max_rows: int = 6, max_width: int = 40, max_block: in
     return Workload(f"random-{seed}", logits, ks if has_starts else None, ke, B, k, R)
 
 
+def many_rows_case(seed: int, rows: int, width: int, block_size: int, row_repeat: int = 1,
+                   topk: int = 8) -> Workload:
+    """Many rows of one width: N(0,1) values with -inf at 1 % and NaN at 0.01 %
+    of the positions; starts uniform in [-B, width / 2], ends uniform in
+    [start - 8, width + B], so windows are empty, ragged, clipped or whole."""
+    rng = _rng(2_000_000 + seed)
+    logits = rng.standard_normal((rows, width), dtype=np.float32)
+    u = rng.random((rows, width), dtype=np.float32)
+    logits[u < 0.01] = -np.inf
+    logits[u < 1e-4] = np.nan
+    groups = -(-rows // row_repeat)
+    ks = rng.integers(-block_size, width // 2, size=groups, endpoint=True)
+    ke = ks + rng.integers(-8, width + block_size, size=groups, endpoint=True)
+    ke = np.clip(ke, 0, width + block_size)
+    return Workload(f"many-rows-{seed}-{rows}x{width}-b{block_size}-r{row_repeat}", logits,
+                    ks.astype(np.int32), ke.astype(np.int32), block_size, topk, row_repeat)
+
+
 def sha256(*arrays) -> str:
     h = hashlib.sha256()
     for a in arrays:

@@ -201,7 +201,7 @@ def test_block_scores(pin):
 
 
 def test_block_scores_configs():
-    for i in (1, 2, 4):
+    for i in (1, 2, 3, 4):
         w = workloads.config(i)
         _say("block scores", w.name)
         x = dev_logits(w.logits)
@@ -211,6 +211,25 @@ def test_block_scores_configs():
             exp = oracle.block_scores(w.logits, w.row_ks, w.row_ke, w.block_size, w.row_repeat,
                                       pin_newest=pin, nthreads=8)
             assert_same(np.zeros(1), got, np.zeros(1), exp, f"{w.name} pin={pin}")
+
+
+@pytest.mark.parametrize("seed,rows,width,B,R", [
+    (1, 1100, 33000, 64, 1),   # >= 1024 rows, >= 32K columns: whole rows, four waves
+    (2, 2048, 32768, 128, 2),
+    (3, 1030, 5003, 7, 1),     # one-wave whole rows on the any-alignment path
+    (4, 1024, 16384, 8, 3),    # one-wave whole rows, vector path
+    (5, 1023, 40000, 16, 1),   # just under 1024 rows: chunks
+])
+def test_block_scores_many_rows(seed, rows, width, B, R):
+    w = workloads.many_rows_case(seed, rows, width, B, R)
+    _say("block scores", w.name)
+    x = dev_logits(w.logits)
+    for pin in (True, False):
+        got = dsa.block_scores(x, dev_i32(w.row_ks), dev_i32(w.row_ke), w.block_size,
+                               w.row_repeat, pin_newest=pin).cpu().numpy()
+        exp = oracle.block_scores(w.logits, w.row_ks, w.row_ke, w.block_size, w.row_repeat,
+                                  pin_newest=pin, nthreads=8)
+        assert_same(np.zeros(1), got, np.zeros(1), exp, f"{w.name} pin={pin}")
 
 
 # ---------------------------------------------------------------- configs ---
