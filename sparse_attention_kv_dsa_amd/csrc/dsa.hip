@@ -1124,8 +1124,13 @@ __global__ void __launch_bounds__(1024) select_pair_rows_kernel(Params p) {
 // loads roll across rounds although the emits are HBM stores: measured on
 // five shapes, the stores' place in the in-order memory counter costs less
 // than the drained rounds did.
+// Six waves per SIMD (at most 80 VGPRs, no spills) against the compiler's
+// 95-97 VGPRs and four or five waves: 8192 one-wave rows of 8192 columns at
+// B = 8 took 30.2 -> 28.1 us; other shapes were unchanged; seven waves spill
+// and lost 10-20 % everywhere.
 template <int G>
-__global__ void __launch_bounds__(kThreads) block_scores_kernel(Params p) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6)))
+block_scores_kernel(Params p) {
   const int wave = wave_index();
   const int nw = blockDim.x >> 6;
   for (int64_t item = blockIdx.x; item < p.items; item += gridDim.x) {
@@ -1149,7 +1154,12 @@ __global__ void __launch_bounds__(kThreads) block_scores_kernel(Params p) {
 // B = global block size, nblocks = max(max_global_blocks, 1).  Columns past
 // min(width, nblocks) are -inf; the pin is floor((e-1)/B) clamped to the
 // last block; rows with e <= 0 select nothing.
-__global__ void __launch_bounds__(1024) select_scores_kernel(Params p) {
+// Seven waves per SIMD (at most 72 VGPRs, no spills): rows' selects share
+// each CU.  On 8192 rows of 1024 scores at k = 64 this took 36.3 -> 31.1 us
+// against the compiler's own choice (83 VGPRs, five waves); six waves gave
+// 32.4, eight spill to scratch and gave 32.0.
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7)))
+select_scores_kernel(Params p) {
   extern __shared__ uint32_t smem[];
   const int wave = wave_index();
   const int nw = blockDim.x >> 6;
