@@ -65,6 +65,17 @@ def test_select_from_scores_random_cases():
         assert np.array_equal(got, exp), (seed, w.scores.shape, w.max_global_blocks, w.topk_blocks)
 
 
+def test_select_from_scores_random_many_rows():
+    """Random DCP cases at up to 9000 rows: the narrow workgroups and the
+    occupancy the kernel is held to at many rows give the oracle's ids."""
+    for seed in range(24):
+        w = workloads.random_scores_case(50_000 + seed, max_rows=(600, 3000, 9000)[seed % 3],
+                                         max_nscore=2500)
+        got = _gpu_sfs(w)
+        exp = _oracle_sfs(w)
+        assert np.array_equal(got, exp), (seed, w.scores.shape, w.max_global_blocks, w.topk_blocks)
+
+
 def test_select_from_scores_full_size():
     w = workloads.dcp_prefill_scores()
     _say("select_from_scores", w.name)

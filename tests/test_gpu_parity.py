@@ -232,6 +232,31 @@ def test_block_scores_many_rows(seed, rows, width, B, R):
         assert_same(np.zeros(1), got, np.zeros(1), exp, f"{w.name} pin={pin}")
 
 
+def test_random_many_rows():
+    """Random shapes around the block scores' plan thresholds (1024 rows,
+    32K columns): scores and ids of every row bit-exact, B from 1 to 300,
+    row_repeat 1-3, k up to 100, windows empty, ragged, clipped or whole."""
+    rng = np.random.default_rng(777)
+    for case in range(40):
+        rows = int(rng.choice([int(rng.integers(1, 200)), int(rng.integers(1000, 1100))]))
+        width = int(rng.integers(1, 40000))
+        B = int(rng.choice([1, 3, 4, 7, 8, 16, 32, 64, 128, 300]))
+        if -(-width // B) > 4096:
+            B = 64
+        R = int(rng.integers(1, 4))
+        k = int(rng.choice([1, 8, 16, 32, 33, 64, 65, 100]))
+        w = workloads.many_rows_case(10_000 + case, rows, width, B, R, k)
+        got, sc = gpu_select(w)
+        exp_out, exp_sc = oracle_select(w)
+        assert_same(got, sc, exp_out, exp_sc, f"case {case} {w.name} k={k}")
+        pin = bool(case % 2)
+        x = dev_logits(w.logits)
+        gs = dsa.block_scores(x, dev_i32(w.row_ks), dev_i32(w.row_ke), B, R,
+                              pin_newest=pin).cpu().numpy()
+        es = oracle.block_scores(w.logits, w.row_ks, w.row_ke, B, R, pin_newest=pin, nthreads=8)
+        assert_same(np.zeros(1), gs, np.zeros(1), es, f"block scores case {case} {w.name}")
+
+
 # ---------------------------------------------------------------- configs ---
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
