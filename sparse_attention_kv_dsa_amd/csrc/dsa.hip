@@ -984,7 +984,9 @@ __global__ void __launch_bounds__(1024) select_group_rows_kernel(Params p) {
 
 // Plan "split", first kernel: item = r * nchunks + c streams blocks
 // [c*chunk_blocks, (c+1)*chunk_blocks) of row r (in-window part only) into
-// the HBM key matrix ws_keys[r, b].
+// the HBM key matrix ws_keys[r, b].  Rolling loads and the full-tile path:
+// 200x262144 40.8 -> 37.5 us, 160x524288 54.6 -> 52.3, 300x524288 100.8 ->
+// 99.1 (whole split steps) against whole rounds with per-unit masks.
 template <int G>
 __global__ void __launch_bounds__(kThreads) stream_keys_kernel(Params p) {
   const int wave = wave_index();
@@ -996,7 +998,7 @@ __global__ void __launch_bounds__(kThreads) stream_keys_kernel(Params p) {
     const int32_t b0 = c * p.chunk_blocks;
     if (b0 >= g.nvb) continue;
     const int32_t b1 = b0 + p.chunk_blocks < g.nvb ? b0 + p.chunk_blocks : g.nvb;
-    stream_blocks<G, kUnroll, false>(p, g, b0, b1, wave, nw, EmitKey{p.ws_keys + r * p.ws_ld});
+    stream_blocks<G, kUnroll, true, true>(p, g, b0, b1, wave, nw, EmitKey{p.ws_keys + r * p.ws_ld});
   }
 }
 
