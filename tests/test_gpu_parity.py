@@ -257,6 +257,26 @@ def test_random_many_rows():
         assert_same(np.zeros(1), gs, np.zeros(1), es, f"block scores case {case} {w.name}")
 
 
+def test_split_plan_long_rows():
+    """The split plan on rows of 20K-300K columns, where its key-streaming
+    kernel meets whole tiles inside the window and rolls its loads across
+    rounds: ids and scores bit-exact for assorted chunk sizes."""
+    rng = np.random.default_rng(4242)
+    for case in range(12):
+        rows = int(rng.integers(1, 300))
+        width = int(rng.integers(20000, 300000))
+        B = int(rng.choice([7, 16, 64, 128]))
+        if -(-width // B) > 4096:
+            B = 128 if -(-width // 128) <= 4096 else 256
+        R = int(rng.integers(1, 4))
+        k = int(rng.choice([1, 16, 32, 64, 65]))
+        w = workloads.many_rows_case(300_000 + case, rows, width, B, R, k)
+        cb = int(rng.choice([0, 32, 64, 256, 1000]))
+        got, sc = gpu_select(w, plan=2, cb=cb)
+        exp_out, exp_sc = oracle_select(w)
+        assert_same(got, sc, exp_out, exp_sc, f"case {case} {w.name} cb={cb}")
+
+
 # ---------------------------------------------------------------- configs ---
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
