@@ -3,26 +3,32 @@
 
 A step is one call of dsa_select_candidate_blocks (windowed block max, pin,
 top-k, ordered -1 padded store; one launch, or two under the split plan) over
-one batch of the chosen synthetic workload, with its inputs already resident
-in HBM.
-The default workload is the decode batch (64 rows x 32768 columns, block 64,
-top-32, row_repeat 2).
+one batch of a synthetic workload, with its inputs already resident in HBM.
+The headline workload is the large packed prefill (8192 rows x 65536
+columns, 2 GiB of logits, block 64, top-64), the largest of the five; the
+decode batch, the prefill chunk and the long-context decode are timed in the
+same run under the same protocol and reported under `per_config`.
 
-Protocol
+Protocol (every workload)
   * inputs are drawn on the host (sparse_attention_kv_dsa_amd.workloads),
-    checked once against the CPU oracle, then copied to M device copies so
-    that >= 2 GiB of logits stream between two uses of the same copy (the
-    256 MB Infinity Cache would otherwise serve them);
-  * W warmup steps, then exactly K steps, captured into a HIP graph (step i
-    uses copy i mod M) and replayed between two synchronisations; HIP events
-    on the replay stream give the time;
+    checked once in full against the CPU oracle (every row, ids and scores),
+    then copied to M device copies (M = --rotate-bytes / matrix size, at
+    least 2);
+  * W warmup steps (step i reads copy i mod M), then five timed regions of
+    exactly K steps each, every region its own HIP graph replayed between two
+    synchronisations; step i of region j reads copy (W + j*K + i) mod M, so
+    the copies keep rotating and no timed step re-reads a copy a warmup step
+    has just read: the 256 MB Infinity Cache cannot serve them.  HIP events
+    on the replay stream time each region; the first region is the reported
+    step time, the five give its spread;
   * value = in-window logits GB/s (algorithmic bytes: only the columns of
     each row's [start, end) window are counted), rows/s beside it;
   * roofline: HBM-bound, achieved = algorithmic bytes per launch / average
-    launch duration, against the 8 TB/s MI355X peak; traffic = per-launch HBM
-    bytes from rocprofv3 counters (profiles/traffic.json) when they were taken
-    on the current kernel source, else null;
-  * cpu_baseline: the oracle (plain C, all host cores) on the same workload.
+    step time, against the 8 TB/s MI355X peak; traffic = per-launch HBM
+    bytes from rocprofv3 counters (profiles/traffic.json) when they were
+    taken on the current kernel source and plan, else null;
+  * cpu_baseline: the oracle (plain C, all host cores) on the headline
+    workload.
 """
 from __future__ import annotations
 
@@ -48,12 +54,17 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
-                    help="workload (1 tiny, 2 decode, 3 prefill, 4 long-context decode, 5 large prefill)")
+    ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5],
+                    help="headline workload (1 tiny, 2 decode, 3 prefill, 4 long-context decode, "
+                         "5 large prefill)")
+    ap.add_argument("--per-config", default="auto",
+                    help="comma list of workloads also timed into per_config ('auto': 2-5 "
+                         "without the headline; 'none': no others)")
     ap.add_argument("--plan", type=int, default=0, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--plan-arg", type=int, default=0,
                     help="plan 1: waves per workgroup; plan 2: blocks per chunk (0: automatic)")
-    ap.add_argument("--rotate-bytes", type=float, default=2.0, help="GiB of input copies to rotate over")
+    ap.add_argument("--rotate-bytes", type=float, default=4.0,
+                    help="GiB of input copies to rotate over (at least two copies)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget (0: skip)")
     ap.add_argument("--eager", action="store_true", help="launch every step from Python, no graph")
     ap.add_argument("--profile", action="store_true",
@@ -218,49 +229,49 @@ def _stream_context(dev, achieved, kind):
     return ctx
 
 
-def _time_steps(launch, K, W, copies, dev, use_graph):
-    """W warmup then K timed steps (step i uses input copy i mod copies),
-    captured in a HIP graph unless use_graph is False; returns ms per step."""
+def _time_steps(launch, K, W, copies, dev, use_graph, regions=5):
+    """W warmup steps (step i reads copy i mod copies), then `regions` timed
+    regions of exactly K steps (step i of region j reads copy
+    (W + j*K + i) mod copies), each region its own HIP graph unless
+    use_graph is False (then one eager region).  Returns ms per step of the
+    first region; _REPEATS holds every region's."""
     import torch
     stream = torch.cuda.current_stream(dev)
+    n_regions = regions if use_graph else 1
     if use_graph:
         cap = torch.cuda.Stream(dev)
-        graphs = {}
-        for name, n in (("warm", W), ("timed", K)):
+
+        def capture(first, n):
             g = torch.cuda.CUDAGraph()
             if n:
                 with torch.cuda.graph(g, stream=cap):
                     for i in range(n):
-                        launch(i % copies)
-            graphs[name] = g
+                        launch((first + i) % copies)
+            return g
+
+        warm = capture(0, W)
+        timed = [capture(W + j * K, K) for j in range(n_regions)]
         torch.cuda.synchronize()
         if W:
-            graphs["warm"].replay()
+            warm.replay()
     else:
         for i in range(W):
             launch(i % copies)
-    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    if use_graph:
-        graphs["timed"].replay()
-    else:
-        for i in range(K):
-            launch(i % copies)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    first = e0.elapsed_time(e1) / K
-    # the reported step time is the region above; four more replays of the
-    # same K steps give its spread
-    _REPEATS[:] = [first]
-    if use_graph:
-        for _ in range(4):
-            e0.record(stream)
-            graphs["timed"].replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            _REPEATS.append(e0.elapsed_time(e1) / K)
-    return first
+    times = []
+    for j in range(n_regions):
+        torch.cuda.synchronize()
+        e0.record(stream)
+        if use_graph:
+            timed[j].replay()
+        else:
+            for i in range(K):
+                launch((W + i) % copies)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / K)
+    _REPEATS[:] = times
+    return times[0]
 
 
 _REPEATS: list = []
@@ -293,7 +304,7 @@ def bench_next(args):
         w = workloads.dcp_prefill_scores()
         rows, nscore = w.scores.shape
         mat = w.scores.nbytes
-        copies = 1 if args.profile else max(1, min(512, int(-(-args.rotate_bytes * 2**30 // mat))))
+        copies = 1 if args.profile else max(2, min(512, int(-(-args.rotate_bytes * 2**30 // mat))))
         xs = [torch.from_numpy(w.scores).to(dev) for _ in range(copies)]
         ke = i32(w.global_row_ke)
         out = torch.empty((rows, w.topk_blocks), dtype=torch.int32, device=dev)
@@ -339,7 +350,7 @@ def bench_next(args):
         sel = np.empty((w.rows, w.topk_blocks), np.int32)
         oracle.select_candidate_blocks(w.logits, w.row_ks, w.row_ke, w.topk_blocks, w.block_size,
                                        sel, w.row_repeat, nthreads=threads)
-        copies = 1 if args.profile else max(1, min(512, int(-(-args.rotate_bytes * 2**30 // w.logits.nbytes))))
+        copies = 1 if args.profile else max(2, min(512, int(-(-args.rotate_bytes * 2**30 // w.logits.nbytes))))
         xs = [torch.from_numpy(w.logits).to(dev) for _ in range(copies)]
         ks, ke, cd = i32(w.row_ks), i32(w.row_ke), i32(sel)
         dsa.mask_candidates(xs[0], ks, ke, cd, w.topk_blocks, w.block_size, w.row_repeat)
@@ -389,7 +400,7 @@ def bench_next(args):
         import oracle
         w = workloads.dcp_local_logits()
         nb = -(-w.width // w.block_size)
-        copies = 1 if args.profile else max(1, min(512, int(-(-args.rotate_bytes * 2**30 // w.logits.nbytes))))
+        copies = 1 if args.profile else max(2, min(512, int(-(-args.rotate_bytes * 2**30 // w.logits.nbytes))))
         xs = [torch.from_numpy(w.logits).to(dev) for _ in range(copies)]
         ks, ke = i32(w.row_ks), i32(w.row_ke)
         sc = torch.empty((w.rows, nb), dtype=torch.float32, device=dev)
@@ -433,7 +444,7 @@ def bench_next(args):
         w = workloads.lse_merge()
         B, H, D = w.out.shape
         N = w.lses.shape[0]
-        copies = 1 if args.profile else max(1, min(64, int(-(-args.rotate_bytes * 2**30 // w.out.nbytes))))
+        copies = 1 if args.profile else max(2, min(64, int(-(-args.rotate_bytes * 2**30 // w.out.nbytes))))
         outs = [torch.from_numpy(w.out).to(dev) for _ in range(copies)]
         lses = torch.from_numpy(w.lses).to(dev)
         new = torch.empty((H, B, D), dtype=torch.float32, device=dev)
@@ -495,74 +506,62 @@ def bench_next(args):
     print(json.dumps(res), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus N > 1 is not "
-                                   "supported (rows would shard across GPUs with no "
-                                   "communication between them)"}))
-        sys.exit(2)
-    if args.op != "select":
-        bench_next(args)
-        return
+KERNELS = {1: "select_group_rows_kernel", 2: "stream_keys_kernel", 3: "select_wave_rows_kernel",
+           4: "select_pair_rows_kernel"}
+
+
+def bench_select(cfg, args, dev, use_graph):
+    """One selection workload under the protocol above: full parity, timing,
+    roofline.  Returns (result dict, workload)."""
     import numpy as np
     import torch
 
+    import oracle
     import sparse_attention_kv_dsa_amd as dsa
-    from sparse_attention_kv_dsa_amd import build as dsa_build
     from sparse_attention_kv_dsa_amd import workloads
 
-    dev = torch.device("cuda:0")
-    w = workloads.config(args.config)
+    w = workloads.config(cfg)
     print(f"# workload {w.name}: drawn", file=sys.stderr, flush=True)
-    nb = -(-w.width // w.block_size)
     plan, cb = dsa.select_plan(w.rows, w.width, w.block_size, w.topk_blocks)
-    if args.plan:
+    if args.plan and cfg == args.config:
         plan, cb = args.plan, args.plan_arg
     L = dsa.lib()
-
+    K, W = args.steps, args.warmup
     ks = None if w.row_ks is None else torch.from_numpy(w.row_ks).to(dev)
     ke = torch.from_numpy(w.row_ke).to(dev)
-    mat_bytes = w.logits.nbytes
-    copies = max(1, min(512, int(-(-args.rotate_bytes * 2**30 // mat_bytes))))
-    if args.profile:
-        copies = 1
+    copies = 1 if args.profile else max(2, min(512, int(-(-args.rotate_bytes * 2**30 //
+                                                          w.logits.nbytes))))
     host = torch.from_numpy(w.logits)
     xs = [host.to(dev) for _ in range(copies)]
     out = torch.empty((w.rows, w.topk_blocks), dtype=torch.int32, device=dev)
+    nb = -(-w.width // w.block_size)
+    sc = torch.empty((w.rows, nb), dtype=torch.float32, device=dev)
     ws = dsa.Workspace(dev, dsa.select_workspace_bytes(w.rows, w.width, w.block_size,
                                                        w.topk_blocks))
     torch.cuda.synchronize()
 
-    # parity once, before timing
+    # parity once, before timing: every row's ids and scores against the oracle
     dsa.select_candidate_blocks(xs[0], ks, ke, w.topk_blocks, w.block_size, out, w.row_repeat,
-                                workspace=ws, plan=plan, plan_arg=cb)
-    got = out.cpu().numpy()
-    parity = None
-    if not args.profile or w.rows <= 128:
-        import oracle
-        exp = np.empty_like(got)
-        if w.rows > 512:   # the oracle checks a row sample on the big prefill workloads
-            rows = np.linspace(0, w.rows - 1, 64).astype(np.int64)
-            sub = workloads.Workload(w.name, np.ascontiguousarray(w.logits[rows]),
-                                     None if w.row_ks is None else w.row_ks[rows].copy(),
-                                     w.row_ke[rows].copy(), w.block_size, w.topk_blocks, 1)
-            exp = np.empty((len(rows), w.topk_blocks), np.int32)
-            oracle.select_candidate_blocks(sub.logits, sub.row_ks, sub.row_ke, sub.topk_blocks,
-                                           sub.block_size, exp, 1, nthreads=8)
-            parity = bool(np.array_equal(got[rows], exp))
-        else:
-            oracle.select_candidate_blocks(w.logits, w.row_ks, w.row_ke, w.topk_blocks,
-                                           w.block_size, exp, w.row_repeat, nthreads=8)
-            parity = bool(np.array_equal(got, exp))
-    print(f"# parity vs oracle: {parity}", file=sys.stderr, flush=True)
+                                scores_out=sc, workspace=ws, plan=plan, plan_arg=cb)
+    got, got_sc = out.cpu().numpy(), sc.cpu().numpy()
+    del sc
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    exp = np.empty_like(got)
+    exp_sc = np.empty_like(got_sc)
+    oracle.select_candidate_blocks(w.logits, w.row_ks, w.row_ke, w.topk_blocks, w.block_size,
+                                   exp, w.row_repeat, scores_out=exp_sc, nthreads=threads)
+    parity = bool(np.array_equal(got, exp) and
+                  np.array_equal(got_sc.view(np.uint32), exp_sc.view(np.uint32)))
+    del exp_sc, got_sc
+    print(f"# {w.name}: parity vs oracle (all {w.rows} rows, ids and scores): {parity}",
+          file=sys.stderr, flush=True)
 
     vp = ctypes.c_void_p
     ks_p = None if ks is None else ks.data_ptr()
 
     def launch(i):
         code = L.dsa_select_candidate_blocks_plan(
-            xs[i % copies].data_ptr(), w.rows, w.width, w.width, ks_p, ke.data_ptr(),
+            xs[i].data_ptr(), w.rows, w.width, w.width, ks_p, ke.data_ptr(),
             w.topk_blocks, w.block_size, w.row_repeat, out.data_ptr(), w.topk_blocks, None, 0,
             ws.buf.data_ptr(), ws.buf.numel(), plan, cb,
             vp(torch.cuda.current_stream(dev).cuda_stream))
@@ -570,62 +569,18 @@ def main():
             raise RuntimeError(f"dsa_select_candidate_blocks: {dsa.status_string(code)}")
 
     _calib_copy(args, dev)
-
-    stream = torch.cuda.current_stream(dev)
-    use_graph = not (args.eager or args.profile)
-    K, W = args.steps, args.warmup
-    if use_graph:
-        cap = torch.cuda.Stream(dev)
-        graphs = {}
-        for name, n in (("warm", W), ("timed", K)):
-            g = torch.cuda.CUDAGraph()
-            if n:
-                with torch.cuda.graph(g, stream=cap):
-                    for i in range(n):
-                        launch(i)
-            graphs[name] = g
-        torch.cuda.synchronize()
-        if W:
-            graphs["warm"].replay()
-    else:
-        for i in range(W):
-            launch(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    if use_graph:
-        graphs["timed"].replay()
-    else:
-        for i in range(K):
-            launch(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / K
-    print(f"# timed {K} steps: {ms * 1e3:.2f} us/step (wall {wall:.3f} s)", file=sys.stderr,
-          flush=True)
-    # the reported step time is the region above; four more replays of the
-    # same K steps give its spread
-    _REPEATS[:] = [ms]
-    if use_graph:
-        for _ in range(4):
-            e0.record(stream)
-            graphs["timed"].replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            _REPEATS.append(e0.elapsed_time(e1) / K)
-    # every launch of the timed region wrote the same ids
+    ms = _time_steps(launch, K, W, copies, dev, use_graph)
+    print(f"# {w.name}: timed {K} steps: {ms * 1e3:.2f} us/step", file=sys.stderr, flush=True)
+    # every launch of the timed regions wrote the checked ids
     assert np.array_equal(out.cpu().numpy(), got), "timed launches disagree with the checked one"
+    del xs
+    torch.cuda.empty_cache()
 
     win = in_window_bytes(w)
     alg = algorithmic_bytes(w)
-    gbps = win / (ms * 1e-3) / 1e9
     achieved = alg / (ms * 1e-3) / 1e9
     res = {
-        "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": K, "warmup": W, "ms_per_step": round(ms, 6), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "value": round(win / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "ms_per_step": round(ms, 6),
         "config": {"workload": w.name, "rows": w.rows, "width": w.width,
                    "block_size": w.block_size, "topk_blocks": w.topk_blocks,
                    "row_repeat": w.row_repeat, "plan": plan, "plan_arg": cb,
@@ -639,13 +594,49 @@ def main():
                      "traffic": traffic_for(w.name, plan),
                      "algorithmic_bytes_per_launch": alg, "in_window_bytes": win,
                      "timed": "whole step (both kernels under the split plan)",
-                     "kernel": {1: "select_group_rows_kernel", 2: "stream_keys_kernel",
-                                3: "select_wave_rows_kernel",
-                                4: "select_pair_rows_kernel"}[plan]},
+                     "kernel": KERNELS[plan]},
     }
+    return res, w
 
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus N > 1 is not "
+                                   "supported (rows would shard across GPUs with no "
+                                   "communication between them)"}))
+        sys.exit(2)
+    if args.op != "select":
+        bench_next(args)
+        return
+    import torch
+
+    dev = torch.device("cuda:0")
+    use_graph = not (args.eager or args.profile)
+    head, w = bench_select(args.config, args, dev, use_graph)
+    others = []
+    if args.per_config == "auto":
+        others = [c for c in (2, 3, 4, 5) if c != args.config]
+    elif args.per_config not in ("", "none"):
+        others = [int(c) for c in args.per_config.split(",") if int(c) != args.config]
+    per = {}
+    for c in others:
+        r, _ = bench_select(c, args, dev, use_graph)
+        per[r["config"]["workload"]] = dict(
+            r["config"], ms_per_step=r["ms_per_step"], value=r["value"], unit=r["unit"],
+            rows_per_s=r["rows_per_s"], parity=r["parity"], repeats=r["repeats"],
+            roofline={k: r["roofline"][k] for k in ("achieved", "frac", "traffic",
+                                                    "algorithmic_bytes_per_launch", "kernel")})
+    res = {"metric": METRIC, "value": head["value"], "unit": head["unit"], "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic"}
+    res.update({k: head[k] for k in ("config", "rows_per_s", "parity", "repeats", "roofline")})
+    res["parity_all"] = bool(head["parity"] and all(v["parity"] for v in per.values()))
+    if per:
+        res["per_config"] = per
     if not args.profile:
-        res["context"] = _stream_context(dev, achieved, "read")
+        res["context"] = _stream_context(dev, head["roofline"]["achieved"], "read")
         if args.cpu_seconds > 0:
             print("# timing the CPU oracle", file=sys.stderr, flush=True)
             res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

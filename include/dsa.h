@@ -30,10 +30,10 @@
  *   out      out[j] for j < topk_blocks: the j-th ranked block id, or -1 when
  *            j >= min(topk_blocks, nblocks) or that block scores -inf.
  *
- * Bounds are device data and are not validated; the kernels never read
- * outside [row, row + min(e, width)) whatever their values, and compute the
- * definition above for any int32 values (the expected use is 0 <= s <= e <=
- * width).
+ * Bounds are device data and are not validated; whatever their values, the
+ * selection and block-score kernels read logits only inside the row's window
+ * [row + max(s, 0), row + min(e, width)), and compute the definition above
+ * for any int32 values (the expected use is 0 <= s <= e <= width).
  *
  * Conventions for every entry point:
  *   - The caller owns every buffer.  The library allocates nothing, keeps no
@@ -41,8 +41,10 @@
  *   - Arguments are checked on the host before anything is enqueued; on any
  *     error the call returns the code and writes nothing.
  *   - `logits` must be 4-byte aligned; a row whose (logits + r*ld_logits + s)
- *     is 16-byte aligned takes the vectorised path, any other row a scalar
- *     path with identical results.
+ *     is 16-byte aligned, with s >= 0 and at least 4 columns in its window,
+ *     takes the vectorised path (16-byte loads of whole in-window groups of
+ *     4 columns, scalar loads for the last 1-3), any other row a scalar path
+ *     with identical results.
  *   - DSA_ERR_HIP: the launch failed (hipGetLastError after the launch).
  */
 #ifndef DSA_H

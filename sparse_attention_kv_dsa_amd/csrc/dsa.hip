@@ -46,6 +46,7 @@
 #include <stdint.h>
 
 #include "dsa.h"
+#include "stream_geom.h"
 
 namespace {
 
@@ -132,7 +133,6 @@ struct Params {
   const int32_t* ke;
   int32_t B, R, pin, k;
   int32_t nblocks, chunk_blocks, nchunks;
-  int32_t vec_ok;      // width % 4 == 0: float4 loads never cross the row's end
   int32_t kcap;        // max(1, min(k, nblocks)): selected-set capacity
   int32_t keys_words;  // LDS words for one row's keys (nblocks rounded up to 4)
   int32_t wave_words;  // LDS words of one row's select state (keys, control, area)
@@ -211,66 +211,73 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Streams blocks [b0, b1) (b1 <= nvb) of a row on the vector path: s >= 0,
-// (row + s) 16-byte aligned and width % 4 == 0, so every float4 that holds an
-// in-window column lies inside the row.  B = 4*G.  The chunk's 1 KiB tiles
-// are dealt to `nw` waves; this is wave `wv`, which takes tiles wv, wv + nw,
-// ... in rounds of U.  Calls emit(b, max) once per block, from one lane of
-// the block.
+// Streams blocks [b0, b1) (b1 <= nvb) of a row on the vector path
+// (dsa_geom::vec_path_ok): B = 4*G, and every float4 loaded is a whole unit
+// of the window (stream_geom.h); the window's partial last unit, if any, is
+// read with up to three scalar loads by the lane that owns it.  The chunk's
+// 1 KiB tiles are dealt to `nw` waves; this is wave `wv`, which takes tiles
+// wv, wv + nw, ... in rounds of U.  Calls emit(b, max) once per block, from
+// one lane of the block.
 //
-// The loads are branch-free: a lane past the chunk's last unit re-reads that
-// unit (same cache line) and masks it.  ROLL: tile j's load for the next
-// round is issued as soon as tile j has been reduced, so U loads stay in
-// flight across rounds instead of draining at each round's end.  Emits into
-// HBM then sit in the same in-order memory counter as the loads; whether
+// The loads are branch-free: a lane past the chunk's last whole unit
+// re-reads that unit and is masked.  ROLL: tile j's load for the next round
+// is issued as soon as tile j has been reduced, so U loads stay in flight
+// across rounds instead of draining at each round's end.  Emits into HBM
+// then sit in the same in-order memory counter as the loads; whether
 // rolling still pays is measured per caller.  FULL: a tile wholly inside the
 // window (a wave-uniform test) skips the per-unit masks.
 template <int G, int U, bool ROLL, bool FULL, class Emit>
 __device__ __forceinline__ void stream_vec(const RowGeom& g, int32_t b0, int32_t b1, int wv,
                                            int nw, const Emit& emit) {
   const int lane = threadIdx.x & 63;
-  const float4* base = reinterpret_cast<const float4*>(g.row + g.s);
-  const int32_t span = (int32_t)(g.hi - g.s);        // in-window columns from s
-  const int32_t nu_row = (span + 3) >> 2;            // units holding one of them
-  const int32_t ub = b0 * G;
-  const int32_t ue = b1 * G < nu_row ? b1 * G : nu_row;
-  const int32_t ntiles = (ue - ub + 63) >> 6;
+  const int32_t span = (int32_t)(g.hi - g.s);  // window columns from s
+  const dsa_geom::VecChunk c = dsa_geom::vec_chunk(span, b0, b1, G);
+  if (wv >= c.ntiles) return;
   const float ninf = -__builtin_inff();
-  const char* cbase = reinterpret_cast<const char*>(base);
+  const char* cbase = reinterpret_cast<const char*>(g.row + g.s);
+  // The partial unit: its owner lane reads its 1-3 columns before the
+  // float4 loads are issued.  Loads return in order, so once the first
+  // tile's float4 has arrived the tail has too; it is then moved to a
+  // scalar register (readlane), which keeps it out of the vector registers
+  // of the streaming loop.
+  float tail_v = ninf;
+  if (c.tail_tile >= 0 && c.tail_tile % nw == wv && lane == c.tail_lane) {
+    const float* tp = g.row + g.s;
+    const float t0 = load_stream(tp + dsa_geom::vec_tail_col(c, 0));
+    const float t1 = load_stream(tp + dsa_geom::vec_tail_col(c, 1));
+    const float t2 = load_stream(tp + dsa_geom::vec_tail_col(c, 2));
+    tail_v = fmaximum(t0, fmaximum(t1, t2));
+  }
+  float tail = ninf;  // wave-uniform: set once the first round is in flight
   // uniform base + 32-bit byte offset: the scalar-base form of the load
   auto load = [&](int32_t t) -> float4 {
-    const int32_t u = ub + (t << 6) + lane;
-    const uint32_t off = (uint32_t)(u < ue ? u : ue - 1) << 4;
+    const uint32_t off = (uint32_t)dsa_geom::vec_load_unit(c, t, lane) << 4;
     return load_stream(static_cast<const void*>(cbase + off));
   };
-  // units [0, full) hold only in-window columns
-  const int32_t full = ue < (span >> 2) ? ue : (span >> 2);
   auto reduce = [&](int32_t t, const float4& x4) {
-    const int32_t u = ub + (t << 6) + lane;
+    const int32_t u = c.ub + (t << 6) + lane;
     float m;
-    if (FULL && ub + (t << 6) + 64 <= full) {  // wave-uniform: the tile is all in the window
+    if (FULL && c.ub + (t << 6) + 64 <= c.full_end) {  // wave-uniform: all whole units
       m = fmaximum(fmaximum(x4.x, x4.y), fmaximum(x4.z, x4.w));
     } else {
-      const int32_t lim = u < ue ? span - 4 * u : 0;  // valid columns in this unit
-      const float x = lim > 0 ? x4.x : ninf;
-      const float y = lim > 1 ? x4.y : ninf;
-      const float z = lim > 2 ? x4.z : ninf;
-      const float w = lim > 3 ? x4.w : ninf;
-      m = fmaximum(fmaximum(x, y), fmaximum(z, w));
+      const int32_t cols = dsa_geom::vec_unit_cols(c, span, u);
+      const float m4 = fmaximum(fmaximum(x4.x, x4.y), fmaximum(x4.z, x4.w));
+      m = cols == 4 ? m4 : (cols > 0 ? tail : ninf);
     }
     m = group_max<G>(m);
-    if (t < ntiles) {
+    if (t < c.ntiles) {
       const int32_t b = b0 + (((t << 6) + lane) / G);
       if ((lane % G) == 0 && b < b1) emit(b, m);
     }
   };
-  if (wv >= ntiles) return;
   const int32_t step = nw * U;
   float4 v[U];
   if constexpr (ROLL) {
-    const int32_t rounds = (ntiles - wv + step - 1) / step;  // wave-uniform, >= 1
+    const int32_t rounds = (c.ntiles - wv + step - 1) / step;  // wave-uniform, >= 1
 #pragma unroll
     for (int j = 0; j < U; ++j) v[j] = load(wv + j * nw);
+    tail = __builtin_bit_cast(
+        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tail_v), c.tail_lane));
     int32_t t0 = wv;
     for (int32_t r = 1; r < rounds; ++r, t0 += step) {
 #pragma unroll
@@ -282,7 +289,9 @@ __device__ __forceinline__ void stream_vec(const RowGeom& g, int32_t b0, int32_t
 #pragma unroll
     for (int j = 0; j < U; ++j) reduce(t0 + j * nw, v[j]);
   } else {
-    for (int32_t t0 = wv; t0 < ntiles; t0 += step) {
+    tail = __builtin_bit_cast(
+        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tail_v), c.tail_lane));
+    for (int32_t t0 = wv; t0 < c.ntiles; t0 += step) {
 #pragma unroll
       for (int j = 0; j < U; ++j) v[j] = load(t0 + j * nw);
 #pragma unroll
@@ -292,9 +301,10 @@ __device__ __forceinline__ void stream_vec(const RowGeom& g, int32_t b0, int32_t
 }
 
 // Any block size and alignment: gl = largest power of two <= min(B, 64)
-// lanes share a block, each striding over the block's in-window columns with
+// lanes share a block, each striding over the block's window columns with
 // scalar loads, four in flight; a masked slot re-reads the block's first
-// in-window column.  Blocks are dealt to `nw` waves; this is wave `wv`.
+// window column (stream_geom.h).  Blocks are dealt to `nw` waves; this is
+// wave `wv`.
 template <class Emit>
 __device__ __forceinline__ void stream_scalar(const RowGeom& g, int32_t B, int32_t b0,
                                               int32_t b1, int wv, int nw, const Emit& emit) {
@@ -307,19 +317,15 @@ __device__ __forceinline__ void stream_scalar(const RowGeom& g, int32_t B, int32
   for (int64_t bb = (int64_t)b0 + (int64_t)wv * per_wave; bb < b1;
        bb += (int64_t)nw * per_wave) {
     const int64_t b = bb + lane / gl;
-    const int64_t cs = g.s + b * B;  // first column of block b
-    const int64_t lo = b < b1 ? (cs > g.lo ? cs : g.lo) : 0;
-    const int64_t hi = b < b1 ? (cs + B < g.hi ? cs + B : g.hi) : 0;
+    const dsa_geom::ScalarBlock blk = dsa_geom::scalar_block(g.s, g.lo, g.hi, b, B, b1);
     float m = ninf;
-    for (int64_t c = lo + sub; c < hi; c += 4 * gl) {
+    for (int64_t c = blk.lo + sub; c < blk.hi; c += 4 * gl) {
       float x[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t cq = c + (int64_t)q * gl;
-        x[q] = load_stream(g.row + (cq < hi ? cq : lo));
-      }
+      for (int q = 0; q < 4; ++q)
+        x[q] = load_stream(g.row + dsa_geom::scalar_load_col(blk, c + (int64_t)q * gl));
 #pragma unroll
-      for (int q = 0; q < 4; ++q) m = fmaximum(m, c + (int64_t)q * gl < hi ? x[q] : ninf);
+      for (int q = 0; q < 4; ++q) m = fmaximum(m, c + (int64_t)q * gl < blk.hi ? x[q] : ninf);
     }
     m = group_max_dyn(m, gl);
     if (sub == 0 && b < b1) emit((int32_t)b, m);
@@ -331,7 +337,7 @@ __device__ __forceinline__ void stream_blocks(const Params& p, const RowGeom& g,
                                               int32_t b1, int wv, int nw, const Emit& emit) {
   if (b1 <= b0) return;
   if constexpr (G > 0) {
-    if (p.vec_ok && g.s >= 0 && ((reinterpret_cast<uintptr_t>(g.row + g.s) & 15u) == 0)) {
+    if (dsa_geom::vec_path_ok(reinterpret_cast<uintptr_t>(g.row + g.s), g.s, g.hi - g.s)) {
       stream_vec<G, U, ROLL, FULL>(g, b0, b1, wv, nw, emit);
       return;
     }
@@ -1635,7 +1641,6 @@ dsa_status_t dsa_block_scores(const float* logits, int64_t rows, int64_t width,
   p.R = row_repeat;
   p.pin = pin_newest;
   p.nblocks = (int32_t)nblocks;
-  p.vec_ok = (width % 4) == 0 && width < ((int64_t)1 << 30);
   // Items are row chunks: 8K columns, doubled until at most 512 items
   // remain (few rows: chunks spread each row over many CUs), or whole rows
   // from 1024 rows on.  Whole rows take one wave below 32K columns (short
@@ -1717,7 +1722,6 @@ dsa_status_t dsa_select_candidate_blocks_plan(
   p.pin = 1;
   p.k = topk_blocks;
   p.nblocks = (int32_t)nblocks;
-  p.vec_ok = (width % 4) == 0 && width < ((int64_t)1 << 30);
   p.kcap = (int32_t)select_kcap(nblocks, topk_blocks);
   p.keys_words = (int32_t)select_keys_words(nblocks);
   p.wave_words = (int32_t)ww;

@@ -1,5 +1,6 @@
-"""bench.py's JSON line on the GPU: one run of the tiny workload and one of
-a row after selection, checked for the fields the line promises."""
+"""bench.py's JSON line on the GPU: short runs of the tiny workload, of the
+decode batch with the long-context decode beside it (per_config), and of
+rows after selection, checked for the fields the line promises."""
 import json
 import os
 import subprocess
@@ -18,7 +19,8 @@ def _run(*args):
     return json.loads(r.stdout.strip().splitlines()[-1])
 
 
-@pytest.mark.parametrize("args", [("--config", "1"), ("--op", "lse"), ("--op", "blockscores")])
+@pytest.mark.parametrize("args", [("--config", "1", "--per-config", "none"), ("--op", "lse"),
+                                  ("--op", "blockscores")])
 def test_bench_line(args):
     d = _run(*args, "--steps", "20", "--warmup", "5", "--cpu-seconds", "0.5",
              "--rotate-bytes", "0.25")
@@ -36,3 +38,15 @@ def test_bench_line(args):
     assert ctx["read_stream_GBps"] > 1000 and ctx["graph_launch_floor_us"] > 0
     rep = d["repeats"]
     assert rep["n"] == 5 and rep["ms_per_step_min"] <= rep["ms_per_step_median"] <= rep["ms_per_step_max"]
+
+
+def test_bench_per_config():
+    d = _run("--config", "2", "--per-config", "4", "--steps", "10", "--warmup", "3",
+             "--cpu-seconds", "0.5", "--rotate-bytes", "0.5")
+    assert d["config"]["workload"].startswith("decode-64x32768") and d["parity"] is True
+    assert d["parity_all"] is True
+    (name, pc), = d["per_config"].items()
+    assert name.startswith("longctx-decode") and pc["parity"] is True
+    assert pc["ms_per_step"] > 0 and pc["plan"] == 4 and pc["input_copies"] >= 2
+    assert abs(pc["roofline"]["frac"] - pc["roofline"]["achieved"] / 8000.0) < 1e-3
+    assert pc["repeats"]["n"] == 5

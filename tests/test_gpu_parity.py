@@ -5,6 +5,8 @@ for bit (the max is exact, NaN is the canonical 0x7FC00000).  Inputs come from
 the seeded generators in sparse_attention_kv_dsa_amd.workloads; expected
 values come only from oracle/.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -27,7 +29,7 @@ def dev_logits(x: np.ndarray, ld_pad: int = 0, offset: int = 0, pad_value=np.nan
     read outside a row's first `width` columns would show up in the results."""
     rows, width = x.shape
     ld = width + ld_pad
-    flat = torch.full((offset + rows * ld + 4,), float(pad_value), dtype=torch.float32, device=DEV)
+    flat = torch.full((offset + rows * ld,), float(pad_value), dtype=torch.float32, device=DEV)
     view = flat[offset:offset + rows * ld].view(rows, ld) if rows else flat[:0].view(0, ld)
     if rows and width:
         view[:, :width].copy_(torch.from_numpy(np.ascontiguousarray(x)))
@@ -70,12 +72,16 @@ def gpu_select(w, plan=0, cb=0, ld_pad=0, offset=0, with_scores=True, ld_out_pad
     return out.cpu().numpy(), (None if sc is None else sc.cpu().numpy())
 
 
-def oracle_select(w, rows=None):
+HOST_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_select(w):
     nb = -(-w.width // w.block_size)
     out = np.empty((w.rows, w.topk_blocks), dtype=np.int32)
     sc = np.empty((w.rows, nb), dtype=np.float32)
     oracle.select_candidate_blocks(w.logits, w.row_ks, w.row_ke, w.topk_blocks, w.block_size,
-                                   out, w.row_repeat, scores_out=sc if nb else None, nthreads=8)
+                                   out, w.row_repeat, scores_out=sc if nb else None,
+                                   nthreads=HOST_THREADS)
     return out, sc
 
 
@@ -307,25 +313,65 @@ def _check_properties(out, nblocks):
         assert len(np.unique(ids)) == n and (ids < nblocks).all(), r
 
 
-def test_config5_sampled_rows():
-    """Large prefill at full size (2 GiB of logits) in the launch plan the
-    benchmark times: every row checked for valid ids, 96 sampled rows (both
-    requests, first/last rows) against the oracle, including their scores."""
+def test_config5_full():
+    """Large prefill at full size (2 GiB of logits, heavy ties) in the launch
+    plan the benchmark times: ids and fp32 scores of all 8192 rows bit-exact
+    against the oracle (run on every host core)."""
     w = workloads.config(5)
-    _say("config 5 generated", w.name)
+    _say("config 5 generated", w.name, "plan", dsa.select_plan(w.rows, w.width, w.block_size,
+                                                                 w.topk_blocks))
     got, sc = gpu_select(w)
+    exp_out, exp_sc = oracle_select(w)
+    assert_same(got, sc, exp_out, exp_sc, "config 5, all rows")
     nb = -(-w.width // w.block_size)
     _check_properties(got, nb)
-    rng = np.random.default_rng(5)
-    rows = np.unique(np.concatenate([[0, 1, 4095, 4096, 4097, 8191],
-                                     rng.choice(8192, size=90, replace=False)]))
-    sub = workloads.Workload(w.name, np.ascontiguousarray(w.logits[rows]), w.row_ks[rows].copy(),
-                             w.row_ke[rows].copy(), w.block_size, w.topk_blocks, 1)
-    exp_out, exp_sc = oracle_select(sub)
-    assert_same(got[rows], sc[rows], exp_out, exp_sc, "config 5 sampled rows")
-    # heavy ties: many selected rows end in a run of equal scores, broken by ascending id
-    s_sel = np.take_along_axis(sc[rows], np.maximum(exp_out, 0), axis=1)
+    # heavy ties: most rows end their selection in a run of equal scores,
+    # broken by ascending block id
+    s_sel = np.take_along_axis(exp_sc, np.maximum(exp_out, 0), axis=1)
     assert (s_sel[:, -1] == s_sel[:, -2]).mean() > 0.5
+    # and the other plans that hold this shape give the same bits
+    for plan, cb in ((3, 0), (2, 0)):
+        got2, sc2 = gpu_select(w, plan=plan, cb=cb)
+        assert_same(got2, sc2, exp_out, exp_sc, f"config 5 plan {plan}")
+
+
+def _abi_select(w, workspace, ws_bytes, scores=False):
+    """dsa_select_candidate_blocks (the automatic-plan entry point) called
+    through ctypes with a caller-owned workspace, on the current stream."""
+    import ctypes
+    x = dev_logits(w.logits)
+    ks, ke = dev_i32(w.row_ks), dev_i32(w.row_ke)
+    nb = -(-w.width // w.block_size)
+    out = torch.full((w.rows, w.topk_blocks), 12345, dtype=torch.int32, device=DEV)
+    sc = torch.full((w.rows, nb), 777.0, dtype=torch.float32, device=DEV) if scores else None
+    code = dsa.lib().dsa_select_candidate_blocks(
+        x.data_ptr(), w.rows, w.width, x.stride(0), None if ks is None else ks.data_ptr(),
+        ke.data_ptr(), w.topk_blocks, w.block_size, w.row_repeat, out.data_ptr(), w.topk_blocks,
+        None if sc is None else sc.data_ptr(), nb if scores else 0, workspace, ws_bytes,
+        ctypes.c_void_p(torch.cuda.current_stream(DEV).cuda_stream))
+    assert code == 0, dsa.status_string(code)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), None if sc is None else sc.cpu().numpy()
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_exported_entry_point(cfg):
+    """The exported dsa_select_candidate_blocks itself (page:
+    select_candidate_blocks, non-DCP branch), not the plan variant: with a
+    zeroed caller workspace (configs 2 and 4 run the pair plan, which uses
+    it, over several calls), and with none (the automatic plan then falls
+    back to one that needs none)."""
+    w = workloads.config(cfg)
+    exp_out, exp_sc = oracle_select(w)
+    need = dsa.select_workspace_bytes(w.rows, w.width, w.block_size, w.topk_blocks)
+    ws = torch.zeros(need + 256, dtype=torch.uint8, device=DEV)
+    base = (ws.data_ptr() + 127) // 128 * 128
+    for i in range(3):
+        got, sc = _abi_select(w, base, need, scores=(i == 0))
+        assert_same(got, sc, exp_out, exp_sc if i == 0 else None, f"{w.name} call {i}")
+    assert int(ws[base - ws.data_ptr():base - ws.data_ptr() + 2048].count_nonzero()) == 0
+    got, sc = _abi_select(w, None, 0, scores=True)
+    assert_same(got, sc, exp_out, exp_sc, f"{w.name} without workspace")
 
 
 # ------------------------------------------------------------ behaviour ----
