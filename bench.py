@@ -71,6 +71,9 @@ def parse():
                     help="short eager run for rocprofv3: no graph, no oracle timing, no context runs")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain copy of this many MiB (counter scale for rocprofv3 --pmc)")
+    ap.add_argument("--keys", action="store_true",
+                    help="with --op scores / blockscores: the uint32-code variants "
+                         "(dsa_select_from_keys / dsa_block_score_keys)")
     ap.add_argument("--op", default="select",
                     choices=["select", "scores", "mask", "lse", "blockscores"],
                     help="select: candidate-block selection (the headline, default); scores: the "
@@ -305,11 +308,14 @@ def bench_next(args):
         rows, nscore = w.scores.shape
         mat = w.scores.nbytes
         copies = 1 if args.profile else max(2, min(512, int(-(-args.rotate_bytes * 2**30 // mat))))
-        xs = [torch.from_numpy(w.scores).to(dev) for _ in range(copies)]
+        # --keys: the same scores as uint32 codes (the reduced matrix of the
+        # integer-maximum reduce), held in int32 tensors
+        host = oracle.score_keys(w.scores).view(np.int32) if args.keys else w.scores
+        xs = [torch.from_numpy(host).to(dev) for _ in range(copies)]
         ke = i32(w.global_row_ke)
         out = torch.empty((rows, w.topk_blocks), dtype=torch.int32, device=dev)
-        dsa.select_from_scores(xs[0], ke, w.topk_blocks, w.global_block_size,
-                               w.max_global_blocks, out)
+        sel = dsa.select_from_keys if args.keys else dsa.select_from_scores
+        sel(xs[0], ke, w.topk_blocks, w.global_block_size, w.max_global_blocks, out)
         torch.cuda.synchronize()
         exp = np.empty((rows, w.topk_blocks), np.int32)
         oracle.select_from_scores(w.scores, w.global_row_ke, w.topk_blocks, w.global_block_size,
@@ -317,15 +323,15 @@ def bench_next(args):
         parity = bool(np.array_equal(out.cpu().numpy(), exp))
 
         def launch(i):
-            dsa.select_from_scores(xs[i], ke, w.topk_blocks, w.global_block_size,
-                                   w.max_global_blocks, out)
+            sel(xs[i], ke, w.topk_blocks, w.global_block_size, w.max_global_blocks, out)
 
         live = int((w.global_row_ke > 0).sum())
         read = live * min(nscore, w.max_global_blocks) * 4
         alg = read + rows * 4 + rows * w.topk_blocks * 4
-        metric = "DCP select-from-scores: score GB/s (fraction of HBM peak), 1 GPU"
+        metric = ("DCP select-from-keys: code GB/s (fraction of HBM peak), 1 GPU" if args.keys
+                  else "DCP select-from-scores: score GB/s (fraction of HBM peak), 1 GPU")
         value_bytes, kernel = read, "select_scores_kernel"
-        cfg = {"workload": w.name, "rows": rows, "nscore": nscore,
+        cfg = {"workload": w.name + ("-codes" if args.keys else ""), "rows": rows, "nscore": nscore,
                "max_global_blocks": w.max_global_blocks, "global_block_size": w.global_block_size,
                "topk_blocks": w.topk_blocks, "input_copies": copies}
 
@@ -355,11 +361,10 @@ def bench_next(args):
         ks, ke, cd = i32(w.row_ks), i32(w.row_ke), i32(sel)
         dsa.mask_candidates(xs[0], ks, ke, cd, w.topk_blocks, w.block_size, w.row_repeat)
         torch.cuda.synchronize()
-        srows = np.linspace(0, w.rows - 1, 64).astype(np.int64)
-        exp = np.ascontiguousarray(w.logits[srows])
-        oracle.mask_candidates(exp, w.row_ks[srows], w.row_ke[srows], np.ascontiguousarray(sel[srows]),
-                               w.topk_blocks, w.block_size, 1)
-        parity = bool(np.array_equal(xs[0].cpu().numpy()[srows].view(np.uint32), exp.view(np.uint32)))
+        exp = w.logits.copy()
+        oracle.mask_candidates(exp, w.row_ks, w.row_ke, sel, w.topk_blocks, w.block_size, 1)
+        parity = bool(np.array_equal(xs[0].cpu().numpy().view(np.uint32), exp.view(np.uint32)))
+        del exp
         # kept columns: in-window columns of selected blocks (neither read nor written)
         kept = 0
         for r in range(w.rows):
@@ -403,23 +408,34 @@ def bench_next(args):
         copies = 1 if args.profile else max(2, min(512, int(-(-args.rotate_bytes * 2**30 // w.logits.nbytes))))
         xs = [torch.from_numpy(w.logits).to(dev) for _ in range(copies)]
         ks, ke = i32(w.row_ks), i32(w.row_ke)
-        sc = torch.empty((w.rows, nb), dtype=torch.float32, device=dev)
-        dsa.block_scores(xs[0], ks, ke, w.block_size, 1, pin_newest=False, out=sc)
+        threads = max(1, min(16, threads))
+        if args.keys:
+            sc = torch.empty((w.rows, nb), dtype=torch.int32, device=dev)
+            run = dsa.block_score_keys
+            exp = oracle.block_score_keys(w.logits, w.row_ks, w.row_ke, w.block_size, 1,
+                                          pin_newest=False, nthreads=threads).view(np.uint32)
+        else:
+            sc = torch.empty((w.rows, nb), dtype=torch.float32, device=dev)
+            run = dsa.block_scores
+            exp = oracle.block_scores(w.logits, w.row_ks, w.row_ke, w.block_size, 1,
+                                      pin_newest=False, nthreads=threads).view(np.uint32)
+        run(xs[0], ks, ke, w.block_size, 1, pin_newest=False, out=sc)
         torch.cuda.synchronize()
-        srows = np.linspace(0, w.rows - 1, 64).astype(np.int64)
-        exp = oracle.block_scores(np.ascontiguousarray(w.logits[srows]), w.row_ks[srows],
-                                  w.row_ke[srows], w.block_size, 1, pin_newest=False)
-        parity = bool(np.array_equal(sc.cpu().numpy()[srows].view(np.uint32), exp.view(np.uint32)))
+        parity = bool(np.array_equal(sc.cpu().numpy().view(np.uint32), exp))   # every row
+        del exp
 
         def launch(i):
-            dsa.block_scores(xs[i], ks, ke, w.block_size, 1, pin_newest=False, out=sc)
+            run(xs[i], ks, ke, w.block_size, 1, pin_newest=False, out=sc)
 
         read = in_window_bytes(w)
         written = w.rows * nb * 4
         alg = read + written + w.rows * 8
-        metric = "DCP local block scores: logits GB/s (fraction of HBM peak), 1 GPU"
+        metric = ("DCP local block score codes: logits GB/s (fraction of HBM peak), 1 GPU"
+                  if args.keys else
+                  "DCP local block scores: logits GB/s (fraction of HBM peak), 1 GPU")
         value_bytes, kernel = read, "block_scores_kernel"
-        cfg = {"workload": w.name, "rows": w.rows, "width": w.width, "block_size": w.block_size,
+        cfg = {"workload": w.name + ("-codes" if args.keys else ""), "rows": w.rows,
+               "width": w.width, "block_size": w.block_size,
                "pin_newest": False, "input_copies": copies, "scores_bytes": written}
 
         def cpu(budget):
@@ -451,12 +467,11 @@ def bench_next(args):
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
         dsa.correct_attn_out(outs[0], lses, w.cp_rank, new_output=new, lse=lse)
         torch.cuda.synchronize()
-        bs = np.arange(0, B, 17)
-        ref_new, ref_lse = oracle.correct_attn_out(np.ascontiguousarray(w.out[bs]),
-                                                   np.ascontiguousarray(w.lses[:, bs]), w.cp_rank)
-        got = new[:, bs].cpu().numpy().astype(np.float64)
+        ref_new, ref_lse = oracle.correct_attn_out(w.out, w.lses, w.cp_rank)
+        got = new.cpu().numpy().astype(np.float64)
         parity = bool(np.allclose(got, ref_new, rtol=1e-5, atol=0) and
-                      np.allclose(lse[bs].cpu().numpy(), ref_lse, rtol=1e-6, atol=1e-5))
+                      np.allclose(lse.cpu().numpy(), ref_lse, rtol=1e-6, atol=1e-5))
+        del ref_new, got
 
         def launch(i):
             dsa.correct_attn_out(outs[i], lses, w.cp_rank, new_output=new, lse=lse)

@@ -87,6 +87,31 @@ dsa_status_t dsa_block_scores(const float* logits, int64_t rows, int64_t width,
                               int64_t ld_scores, hipStream_t stream);
 
 /*
+ * dsa_block_scores with every score written as its order-preserving uint32
+ * code instead of fp32: the form in which the local block scores of the
+ * page's decode-context-parallel branch (_select_candidate_blocks_impl, DCP
+ * branch: unpinned local scores, then an all-reduce MAX over the ranks)
+ * reduce exactly by an integer maximum, whatever a collective does with
+ * floats.  The code of a score x:
+ *   x NaN (any sign or payload)   -> 0xFFC00000 (the code of 0x7FC00000);
+ *   sign bit of x clear (+0, ...)  -> bits(x) | 0x80000000;
+ *   sign bit of x set (-0, ...)    -> ~bits(x).
+ * Unsigned order of codes is the order of the IEEE-754-2019 maximum the
+ * scores use (NaN above +inf, +0 above -0), so max(code(a), code(b)) ==
+ * code(maximum(a, b)).  -inf (a block with no element) is 0x007FFFFF, a
+ * pinned block 0xFF800000.
+ *
+ *   keys     uint32 [rows, ld_keys], ld_keys >= nblocks; every b < nblocks of
+ *            every row is written.
+ * Arguments, early exits and errors as dsa_block_scores.
+ */
+dsa_status_t dsa_block_score_keys(const float* logits, int64_t rows, int64_t width,
+                                  int64_t ld_logits, const int32_t* row_ks,
+                                  const int32_t* row_ke, int32_t block_size,
+                                  int32_t row_repeat, int32_t pin_newest, uint32_t* keys,
+                                  int64_t ld_keys, hipStream_t stream);
+
+/*
  * Bytes of device workspace the split and pair plans of
  * dsa_select_candidate_blocks need for this shape: 2048 bytes of per-row
  * arrival counters (pair plan, up to 256 rows), then one uint32 score key
@@ -182,8 +207,9 @@ dsa_status_t dsa_select_candidate_blocks_plan(
 dsa_status_t dsa_select_plan(int64_t rows, int64_t width, int32_t block_size,
                              int32_t topk_blocks, int32_t* plan, int32_t* plan_arg);
 
-/* Static string naming a status code ("DSA_OK", ...); "unknown" otherwise. */
-const char* dsa_status_string(dsa_status_t status);
+/* Static string naming a status code ("DSA_OK", ...); "unknown" for any
+ * other int value. */
+const char* dsa_status_string(int status);
 
 /*
  * Selection from a reduced block-score matrix: the part of the page's
@@ -216,6 +242,26 @@ dsa_status_t dsa_select_from_scores(const float* scores, int64_t rows, int64_t n
                                     const int32_t* global_row_ke, int32_t row_repeat,
                                     int32_t global_block_size, int32_t topk_blocks, int32_t* out,
                                     int64_t ld_out, hipStream_t stream);
+
+/*
+ * dsa_select_from_scores on a matrix of the uint32 codes that
+ * dsa_block_score_keys writes (after the ranks' codes are reduced with an
+ * integer maximum): the same pin, e <= 0 rule, ranking and -1 padded output,
+ * for the scores the codes stand for.  A code that dsa_block_score_keys
+ * never writes (above 0xFF800000 or below 0x007FFFFF: the codes of NaNs with
+ * other payloads or signs) stands for NaN, as every NaN does in
+ * dsa_select_from_scores.
+ *
+ *   keys   uint32 [rows, ld_keys], nkeys columns; may be NULL when
+ *          nkeys == 0.
+ * Arguments, early exits and errors as dsa_select_from_scores (nkeys and
+ * ld_keys in the places of nscore and ld_scores).
+ */
+dsa_status_t dsa_select_from_keys(const uint32_t* keys, int64_t rows, int64_t nkeys,
+                                  int64_t ld_keys, int64_t max_global_blocks,
+                                  const int32_t* global_row_ke, int32_t row_repeat,
+                                  int32_t global_block_size, int32_t topk_blocks, int32_t* out,
+                                  int64_t ld_out, hipStream_t stream);
 
 /*
  * Candidate masking of packed logits, in place (page: the masking function

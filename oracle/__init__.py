@@ -49,6 +49,14 @@ def _open(path):
     lib.oracle_select_candidate_blocks.restype = ctypes.c_int
     lib.oracle_select_from_scores.argtypes = [vp, i64, i64, i64, i64, vp, i32, i32, i32, vp, i64]
     lib.oracle_select_from_scores.restype = ctypes.c_int
+    lib.oracle_score_key.argtypes = [ctypes.c_float]
+    lib.oracle_score_key.restype = ctypes.c_uint32
+    lib.oracle_key_score.argtypes = [ctypes.c_uint32]
+    lib.oracle_key_score.restype = ctypes.c_float
+    lib.oracle_score_keys.argtypes = [vp, i64, i64, i64, vp, i64]
+    lib.oracle_score_keys.restype = ctypes.c_int
+    lib.oracle_select_from_keys.argtypes = [vp, i64, i64, i64, i64, vp, i32, i32, i32, vp, i64]
+    lib.oracle_select_from_keys.restype = ctypes.c_int
     lib.oracle_mask_candidates.argtypes = [vp, i64, i64, i64, vp, vp, vp, i64, i32, i32, i32]
     lib.oracle_mask_candidates.restype = ctypes.c_int
     lib.oracle_correct_attn_out.argtypes = ([vp] + [i64] * 6 + [vp] + [i64] * 5 + [vp] + [i64] * 3
@@ -165,6 +173,49 @@ def select_from_scores(scores: np.ndarray, global_row_ke, topk_blocks: int,
     rc = _load().oracle_select_from_scores(_ptr(scores), rows, nscore, ld, max_global_blocks,
                                            _ptr(ends), row_repeat, global_block_size,
                                            topk_blocks, _ptr(out), _ld(out))
+    assert rc == 0
+
+
+def score_key(x: float) -> int:
+    """Order-preserving uint32 code of one fp32 score (see oracle.c)."""
+    return int(_load().oracle_score_key(float(x)))
+
+
+def key_score(k: int) -> float:
+    """The score a code stands for (the canonical NaN for the NaN code)."""
+    return float(_load().oracle_key_score(int(k)))
+
+
+def score_keys(scores: np.ndarray) -> np.ndarray:
+    """uint32 codes of an fp32 [rows, n] matrix, element by element."""
+    assert scores.dtype == np.float32 and scores.ndim == 2
+    rows, n = scores.shape
+    keys = np.empty((rows, n), dtype=np.uint32)
+    if rows and n:
+        rc = _load().oracle_score_keys(_ptr(scores), rows, n, _ld(scores), _ptr(keys), n)
+        assert rc == 0
+    return keys
+
+
+def block_score_keys(logits: np.ndarray, row_ks, row_ke, block_size: int, row_repeat: int = 1,
+                     pin_newest: bool = True, nthreads: int = 1) -> np.ndarray:
+    """uint32 codes of the block scores [rows, ceil(width/block_size)]."""
+    return score_keys(block_scores(logits, row_ks, row_ke, block_size, row_repeat, pin_newest,
+                                   nthreads))
+
+
+def select_from_keys(keys: np.ndarray, global_row_ke, topk_blocks: int, global_block_size: int,
+                     max_global_blocks: int, out: np.ndarray, row_repeat: int = 1) -> None:
+    """select_from_scores on a uint32 [rows, nkeys] matrix of score codes."""
+    assert keys.dtype == np.uint32 and keys.ndim == 2
+    rows, nkeys = keys.shape
+    ends = np.ascontiguousarray(global_row_ke, dtype=np.int32).reshape(-1)
+    assert ends.size >= (-(-rows // row_repeat) if rows else 0)
+    assert out.dtype == np.int32 and out.shape[0] == rows and out.shape[1] >= topk_blocks
+    ld = _ld(keys) if nkeys else 1
+    rc = _load().oracle_select_from_keys(_ptr(keys), rows, nkeys, ld, max_global_blocks,
+                                         _ptr(ends), row_repeat, global_block_size, topk_blocks,
+                                         _ptr(out), _ld(out))
     assert rc == 0
 
 

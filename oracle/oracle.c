@@ -33,8 +33,10 @@
  *
  * Also defined below, each with its source: the selection from a reduced
  * block-score matrix under decode context parallelism (oracle_select_from_
- * scores), the candidate masking of packed logits (oracle_mask_candidates)
- * and the base-2 log-sum-exp correction of partial attention outputs
+ * scores), the order-preserving uint32 codes of block scores that make that
+ * reduce exact on integers (oracle_score_key, oracle_select_from_keys), the
+ * candidate masking of packed logits (oracle_mask_candidates) and the
+ * base-2 log-sum-exp correction of partial attention outputs
  * (oracle_correct_attn_out, page 3).
  *
  * Parity status: block scores, pin and the ordered select are pinned by the
@@ -319,13 +321,73 @@ int oracle_select_from_scores(const float* scores, int64_t rows, int64_t nscore,
     qsort(order, (size_t)nblocks, sizeof(ranked_t), rank_cmp);
     int32_t* o = out + r * ld_out;
     for (int64_t q = 0; q < topk; ++q) {
-      const int minus_inf = isinf(order[q].score) && order[q].score < 0;
-      o[q] = (q < kk && !minus_inf) ? order[q].id : -1;
+      /* slots past k' = min(k, nblocks) are -1; order[] holds nblocks entries */
+      const int in_k = q < kk;
+      o[q] = (in_k && !(isinf(order[q].score) && order[q].score < 0)) ? order[q].id : -1;
     }
   }
   free(full);
   free(order);
   return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Block scores as order-preserving uint32 codes, for an exact integer reduce.
+ *
+ * Source: the same page, DCP branch of _select_candidate_blocks_impl: the
+ * ranks' unpinned local block scores are combined by an all-reduce MAX, which
+ * must keep the scores' own maximum (NaN propagates, +0 beats -0).  Carried
+ * as integers, that reduce is exact whatever a collective does with floats,
+ * provided each score is first mapped to a code whose unsigned order is the
+ * order of that maximum.  The code used here (this project's choice; the
+ * page reduces floats):
+ *   NaN (any sign or payload)        -> 0xFFC00000, the code of 0x7FC00000;
+ *   x with the sign bit clear (+0..) -> bits(x) + 0x80000000;
+ *   x with the sign bit set (-0..)   -> 0xFFFFFFFF - bits(x).
+ * Negatives then fall below every non-negative, larger magnitudes of
+ * negatives lower; -0 sits just below +0; +inf below the NaN code.
+ */
+uint32_t oracle_score_key(float x) {
+  uint32_t u;
+  if (isnan(x)) return 0xFFC00000u;
+  memcpy(&u, &x, sizeof u);
+  if (signbit(x)) return 0xFFFFFFFFu - u;
+  return u + 0x80000000u;
+}
+
+/* The inverse of oracle_score_key (a NaN code gives the canonical NaN). */
+float oracle_key_score(uint32_t k) {
+  uint32_t u = k >= 0x80000000u ? k - 0x80000000u : 0xFFFFFFFFu - k;
+  float x;
+  memcpy(&x, &u, sizeof x);
+  return x;
+}
+
+/* codes[i] = oracle_score_key(scores[i]) for a [rows, n] matrix. */
+int oracle_score_keys(const float* scores, int64_t rows, int64_t n, int64_t ld_scores,
+                      uint32_t* keys, int64_t ld_keys) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < n; ++b)
+      keys[r * ld_keys + b] = oracle_score_key(scores[r * ld_scores + b]);
+  return 0;
+}
+
+/* oracle_select_from_scores on a matrix of codes: every code is turned back
+ * into its score, then the selection runs unchanged. */
+int oracle_select_from_keys(const uint32_t* keys, int64_t rows, int64_t nkeys, int64_t ld_keys,
+                            int64_t max_global_blocks, const int32_t* global_ends,
+                            int32_t row_repeat, int32_t global_block_size, int32_t topk,
+                            int32_t* out, int64_t ld_out) {
+  if (rows <= 0) return 0;
+  int64_t n = nkeys > 0 ? nkeys : 0;
+  float* scores = (float*)malloc(sizeof(float) * (size_t)(rows * n > 0 ? rows * n : 1));
+  if (!scores) return 1;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < n; ++b) scores[r * n + b] = oracle_key_score(keys[r * ld_keys + b]);
+  int rc = oracle_select_from_scores(scores, rows, n, n > 0 ? n : 1, max_global_blocks, global_ends,
+                                     row_repeat, global_block_size, topk, out, ld_out);
+  free(scores);
+  return rc;
 }
 
 /* ------------------------------------------------------------------------

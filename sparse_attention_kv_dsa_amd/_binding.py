@@ -59,6 +59,12 @@ def lib() -> ctypes.CDLL:
                 L.dsa_select_from_scores.argtypes = [vp, i64, i64, i64, i64, vp, i32, i32, i32,
                                                      vp, i64, vp]
                 L.dsa_select_from_scores.restype = ctypes.c_int
+                L.dsa_block_score_keys.argtypes = [vp, i64, i64, i64, vp, vp, i32, i32, i32, vp,
+                                                   i64, vp]
+                L.dsa_block_score_keys.restype = ctypes.c_int
+                L.dsa_select_from_keys.argtypes = [vp, i64, i64, i64, i64, vp, i32, i32, i32,
+                                                   vp, i64, vp]
+                L.dsa_select_from_keys.restype = ctypes.c_int
                 L.dsa_mask_candidates.argtypes = [vp, i64, i64, i64, vp, vp, vp, i64, i32, i32,
                                                   i32, vp]
                 L.dsa_mask_candidates.restype = ctypes.c_int
@@ -124,19 +130,40 @@ def select_plan(rows: int, width: int, block_size: int, topk_blocks: int) -> tup
     return plan.value, cb.value
 
 
+def _capturing(device) -> bool:
+    return torch.cuda.is_current_stream_capturing()
+
+
 class Workspace:
     """Device scratch for the split and pair plans of
     dsa_select_candidate_blocks: allocated zeroed (the pair plan's arrival
     counters must start at zero; every call leaves them zero), one per stream
     that may run concurrently.  Calls whose plan is another one get no
-    default workspace."""
+    default workspace.
+
+    Graph capture: a captured call keeps the address of the buffer it was
+    captured with, so a workspace never frees a buffer it replaces (a graph
+    captured earlier may still replay into it), and it refuses to allocate
+    or grow while the current stream is capturing: size it before capture
+    (select_workspace_bytes gives the size)."""
 
     def __init__(self, device, nbytes: int = 0):
         self.device = torch.device(device)
+        if _capturing(self.device):
+            raise RuntimeError("dsa.Workspace: cannot allocate while a HIP graph is being "
+                               "captured; create it (sized with select_workspace_bytes) before "
+                               "capture")
         self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        self._replaced: list = []
 
     def ensure(self, nbytes: int) -> "Workspace":
         if nbytes > self.buf.numel():
+            if _capturing(self.device):
+                raise RuntimeError(
+                    f"dsa.Workspace: {nbytes} bytes needed but {self.buf.numel()} held, and a "
+                    "HIP graph is being captured; size the workspace before capture "
+                    "(select_workspace_bytes)")
+            self._replaced.append(self.buf)   # an earlier graph may still use it
             self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
         return self
 
@@ -168,6 +195,32 @@ def block_scores(logits: torch.Tensor, row_ks: torch.Tensor | None, row_ke: torc
                                   row_repeat, int(bool(pin_newest)), _ptr(out), _ld(out),
                                   _stream(logits.device))
     _raise(code, "dsa_block_scores")
+    return out
+
+
+def block_score_keys(logits: torch.Tensor, row_ks: torch.Tensor | None, row_ke: torch.Tensor,
+                     block_size: int, row_repeat: int = 1, pin_newest: bool = True,
+                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """Block scores as order-preserving uint32 codes [rows, ceil(width / block_size)]
+    (dsa_block_score_keys): an integer maximum over codes is the scores' own
+    maximum, NaN and +-0 included.  ``out`` may be uint32 or int32 (bit
+    patterns).  torch has no uint32 maximum: to reduce with torch, view the
+    codes as int32 and flip the sign bit (``c ^ -2**31``), whose signed order
+    is the codes' unsigned order."""
+    ld = _check_logits(logits)
+    rows, width = logits.shape
+    nblocks = -(-width // block_size) if block_size > 0 else 0
+    if out is None:
+        out = torch.empty((rows, nblocks), dtype=torch.uint32, device=logits.device)
+    if out.dtype not in (torch.uint32, torch.int32) or out.device != logits.device:
+        raise ValueError("out must be uint32 or int32 on the logits' device")
+    groups = -(-rows // row_repeat) if row_repeat > 0 else 0
+    ks = _bounds(row_ks, "row_ks", groups, logits.device)
+    ke = _bounds(row_ke, "row_ke", groups, logits.device)
+    code = lib().dsa_block_score_keys(_ptr(logits), rows, width, ld, _ptr(ks), _ptr(ke),
+                                      block_size, row_repeat, int(bool(pin_newest)), _ptr(out),
+                                      _ld(out), _stream(logits.device))
+    _raise(code, "dsa_block_score_keys")
     return out
 
 
@@ -238,6 +291,26 @@ def select_from_scores(scores: torch.Tensor, global_row_ke: torch.Tensor, topk_b
                                         global_block_size, topk_blocks, _ptr(out), _ld(out),
                                         _stream(scores.device))
     _raise(code, "dsa_select_from_scores")
+
+
+def select_from_keys(keys: torch.Tensor, global_row_ke: torch.Tensor, topk_blocks: int,
+                     global_block_size: int, max_global_blocks: int, out: torch.Tensor,
+                     row_repeat: int = 1) -> None:
+    """DCP selection after an integer-maximum reduce of uint32 score codes
+    (dsa_select_from_keys): ``keys`` uint32 or int32 (bit patterns)
+    [rows, nkeys]; otherwise as select_from_scores."""
+    if keys.dtype not in (torch.uint32, torch.int32) or keys.device.type != "cuda":
+        raise ValueError("keys must be uint32 or int32 on a HIP device")
+    rows, nkeys = keys.shape
+    ld = _ld(keys) if nkeys else 1
+    if out.dtype != torch.int32 or out.device != keys.device or out.shape[0] != rows:
+        raise ValueError("out must be int32 [rows, >= topk_blocks] on the keys' device")
+    groups = -(-rows // row_repeat) if row_repeat > 0 else 0
+    ke = _bounds(global_row_ke, "global_row_ke", groups, keys.device)
+    code = lib().dsa_select_from_keys(_ptr(keys) if nkeys else None, rows, nkeys, ld,
+                                      max_global_blocks, _ptr(ke), row_repeat, global_block_size,
+                                      topk_blocks, _ptr(out), _ld(out), _stream(keys.device))
+    _raise(code, "dsa_select_from_keys")
 
 
 def mask_candidates(logits: torch.Tensor, row_ks: torch.Tensor | None, row_ke: torch.Tensor,

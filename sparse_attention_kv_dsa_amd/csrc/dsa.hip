@@ -358,6 +358,14 @@ struct EmitScore {
   }
 };
 
+struct EmitScoreKey {  // the same scores as order-preserving uint32 codes
+  uint32_t* row;
+  int32_t pin;
+  __device__ void operator()(int32_t b, float m) const {
+    row[b] = b == pin ? kKeyPosInf : order_key(m);
+  }
+};
+
 // ---------------------------------------------------------------- select --
 //
 // Top-k of one row's block keys, in four steps with no sort of the whole row:
@@ -1128,7 +1136,10 @@ __global__ void __launch_bounds__(1024) select_pair_rows_kernel(Params p) {
 }
 
 // Block scores to HBM; item = r * nchunks + c covers blocks
-// [c*chunk_blocks, (c+1)*chunk_blocks) of row r, in-window or not.  The
+// [c*chunk_blocks, (c+1)*chunk_blocks) of row r, in-window or not.  KEYS:
+// the scores are written as their order-preserving uint32 codes (p.scores
+// then points at uint32 storage), the form in which scores of several
+// context-parallel ranks reduce exactly by an integer maximum.  The
 // loads roll across rounds although the emits are HBM stores: measured on
 // five shapes, the stores' place in the in-order memory counter costs less
 // than the drained rounds did.
@@ -1136,7 +1147,7 @@ __global__ void __launch_bounds__(1024) select_pair_rows_kernel(Params p) {
 // 95-97 VGPRs and four or five waves: 8192 one-wave rows of 8192 columns at
 // B = 8 took 30.2 -> 28.1 us; other shapes were unchanged; seven waves spill
 // and lost 10-20 % everywhere.
-template <int G>
+template <int G, bool KEYS>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6)))
 block_scores_kernel(Params p) {
   const int wave = wave_index();
@@ -1147,17 +1158,26 @@ block_scores_kernel(Params p) {
     const RowGeom g = row_geom(p, r, p.pin != 0);
     const int32_t b0 = c * p.chunk_blocks;
     const int32_t b1 = b0 + p.chunk_blocks < p.nblocks ? b0 + p.chunk_blocks : p.nblocks;
-    float* srow = p.scores + r * p.ld_scores;
     const int32_t sb1 = b1 < g.nvb ? b1 : g.nvb;
-    stream_blocks<G, kUnroll, true, true>(p, g, b0, sb1, wave, nw, EmitScore{srow, g.pin});
     const int32_t f0 = b0 > g.nvb ? b0 : g.nvb;
-    for (int32_t b = f0 + (int32_t)threadIdx.x; b < b1; b += (int32_t)blockDim.x)
-      srow[b] = b == g.pin ? __builtin_inff() : -__builtin_inff();
+    if constexpr (KEYS) {
+      uint32_t* krow = reinterpret_cast<uint32_t*>(p.scores) + r * p.ld_scores;
+      stream_blocks<G, kUnroll, true, true>(p, g, b0, sb1, wave, nw, EmitScoreKey{krow, g.pin});
+      for (int32_t b = f0 + (int32_t)threadIdx.x; b < b1; b += (int32_t)blockDim.x)
+        krow[b] = b == g.pin ? kKeyPosInf : kKeyNegInf;
+    } else {
+      float* srow = p.scores + r * p.ld_scores;
+      stream_blocks<G, kUnroll, true, true>(p, g, b0, sb1, wave, nw, EmitScore{srow, g.pin});
+      for (int32_t b = f0 + (int32_t)threadIdx.x; b < b1; b += (int32_t)blockDim.x)
+        srow[b] = b == g.pin ? __builtin_inff() : -__builtin_inff();
+    }
   }
 }
 
 // Selection from a reduced block-score matrix (the decode-context-parallel
-// branch after its all-reduce): one workgroup per row.  Params reuse:
+// branch after its all-reduce): one workgroup per row.  KEYS: the matrix
+// holds order-preserving uint32 codes instead of fp32 scores (read through
+// the same pointer).  Params reuse:
 // logits = scores [rows, ld] holding `width` columns, ke = global ends,
 // B = global block size, nblocks = max(max_global_blocks, 1).  Columns past
 // min(width, nblocks) are -inf; the pin is floor((e-1)/B) clamped to the
@@ -1166,6 +1186,7 @@ block_scores_kernel(Params p) {
 // each CU.  On 8192 rows of 1024 scores at k = 64 this took 36.3 -> 31.1 us
 // against the compiler's own choice (83 VGPRs, five waves); six waves gave
 // 32.4, eight spill to scratch and gave 32.0.
+template <bool KEYS>
 __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7)))
 select_scores_kernel(Params p) {
   extern __shared__ uint32_t smem[];
@@ -1192,16 +1213,22 @@ select_scores_kernel(Params p) {
     select_row_prepare(ctl, area, threadIdx.x, blockDim.x);
     const int32_t nt = (int32_t)blockDim.x;
     for (int32_t b0 = 0; b0 < g.nvb; b0 += 4 * nt) {  // four loads in flight per lane
-      float v[4];
+      uint32_t v[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int32_t b = b0 + j * nt + (int32_t)threadIdx.x;
-        v[j] = g.row[b < g.nvb ? b : g.nvb - 1];
+        const int32_t bc = b < g.nvb ? b : g.nvb - 1;
+        if constexpr (KEYS) {  // codes of any NaN stand for the canonical NaN's
+          const uint32_t k = reinterpret_cast<const uint32_t*>(g.row)[bc];
+          v[j] = (k > kKeyPosInf || k < kKeyNegInf) ? kKeyNaN : k;
+        } else {
+          v[j] = order_key(g.row[bc]);
+        }
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int32_t b = b0 + j * nt + (int32_t)threadIdx.x;
-        if (b < g.nvb) smem[b] = order_key(v[j]);
+        if (b < g.nvb) smem[b] = v[j];
       }
     }
     __syncthreads();
@@ -1470,7 +1497,21 @@ DSA_KERNEL_TABLE(stream_keys_kernel)
   }
 DSA_PAIR_TABLE(select_pair_rows_ptr, false)
 DSA_PAIR_TABLE(select_pair_rows_full_ptr, true)
-DSA_KERNEL_TABLE(block_scores_kernel)
+#define DSA_SCORES_TABLE(NAME, KEYS)                                                  \
+  void* NAME(int g) {                                                                 \
+    switch (g) {                                                                      \
+      case 1: return reinterpret_cast<void*>(&block_scores_kernel<1, KEYS>);          \
+      case 2: return reinterpret_cast<void*>(&block_scores_kernel<2, KEYS>);          \
+      case 4: return reinterpret_cast<void*>(&block_scores_kernel<4, KEYS>);          \
+      case 8: return reinterpret_cast<void*>(&block_scores_kernel<8, KEYS>);          \
+      case 16: return reinterpret_cast<void*>(&block_scores_kernel<16, KEYS>);        \
+      case 32: return reinterpret_cast<void*>(&block_scores_kernel<32, KEYS>);        \
+      case 64: return reinterpret_cast<void*>(&block_scores_kernel<64, KEYS>);        \
+      default: return reinterpret_cast<void*>(&block_scores_kernel<0, KEYS>);         \
+    }                                                                                 \
+  }
+DSA_SCORES_TABLE(block_scores_kernel_ptr, false)
+DSA_SCORES_TABLE(block_keys_kernel_ptr, true)
 
 // Launches `fn` over `items` work items with `threads` per workgroup and
 // `per_group` items per workgroup.
@@ -1492,7 +1533,8 @@ bool misaligned(const void* ptr, uintptr_t a) {
   return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) != 0;
 }
 
-int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// ceil(a / b) for a >= 0, b >= 1, with no overflow for any such a.
+int64_t cdiv(int64_t a, int64_t b) { return a / b + (a % b != 0 ? 1 : 0); }
 
 int64_t select_kcap(int64_t nblocks, int32_t k) {
   const int64_t kc = k < nblocks ? k : nblocks;
@@ -1525,9 +1567,10 @@ int64_t ws_row_words(int64_t nblocks) { return cdiv(nblocks, 32) * 32; }
 // Chunk size for split rows: aim at ~2048 workgroups in total, 8K-32K columns
 // each, and a multiple of the blocks one wave instruction covers.
 int32_t auto_chunk_blocks(int64_t rows, int64_t width, int32_t B) {
-  int64_t cols = rows > 0 ? (rows * width) / 2048 : width;
-  if (cols < 8192) cols = 8192;
-  if (cols > 32768) cols = 32768;
+  // rows * width / 2048 clamped to [8192, 32768], in 128-bit arithmetic
+  // (the product of two int64 arguments may not fit in 64 bits)
+  const __int128 want = rows > 0 ? ((__int128)rows * width) / 2048 : (__int128)width;
+  const int64_t cols = want < 8192 ? 8192 : (want > 32768 ? 32768 : (int64_t)want);
   int64_t cb = cdiv(cols, B);
   const int g = lanes_per_block(B);
   if (g > 0) {
@@ -1555,8 +1598,8 @@ void pair_shape(int64_t rows, int64_t width, int* parts, int* waves) {
 
 extern "C" {
 
-const char* dsa_status_string(dsa_status_t status) {
-  switch (status) {
+const char* dsa_status_string(int status) {
+  switch (status) {  // any int: callers may pass codes this library never returns
     case DSA_OK: return "DSA_OK";
     case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG";
     case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED";
@@ -1570,6 +1613,8 @@ size_t dsa_select_workspace_bytes(int64_t rows, int64_t width, int32_t block_siz
                                   int32_t topk_blocks) {
   if (rows <= 0 || width <= 0 || block_size < 1 || topk_blocks < 0) return 0;
   const int64_t nblocks = cdiv(width, block_size);
+  // shapes no plan holds (a row's keys must fit in LDS): nothing to size
+  if (rows > INT32_MAX || nblocks > (int64_t)kLdsLimit / 4) return 0;
   return kCountBytes + (size_t)rows * (size_t)ws_row_words(nblocks) * 4u;
 }
 
@@ -1595,7 +1640,7 @@ dsa_status_t dsa_select_plan(int64_t rows, int64_t width, int32_t block_size,
     pair_shape(rows, width, &parts, &waves);
     *plan = kPlanPair;
     *plan_arg = waves | parts << 8;
-  } else if (rows * 1024 >= width || width <= 32768) {
+  } else if (rows >= cdiv(width, 1024) || width <= 32768) {  // rows * 1024 >= width
     // Rows of up to 32K columns, or enough rows to keep HBM busy one CU per
     // row (256 rows of 256K columns): 8 or 16 waves stream each row, the
     // select fused behind them in the same launch.  Measured against the
@@ -1615,11 +1660,16 @@ dsa_status_t dsa_select_plan(int64_t rows, int64_t width, int32_t block_size,
   return DSA_OK;
 }
 
-dsa_status_t dsa_block_scores(const float* logits, int64_t rows, int64_t width,
-                              int64_t ld_logits, const int32_t* row_ks,
-                              const int32_t* row_ke, int32_t block_size,
-                              int32_t row_repeat, int32_t pin_newest, float* scores,
-                              int64_t ld_scores, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// dsa_block_scores / dsa_block_score_keys: `scores` is fp32 or, with keys,
+// uint32 storage.
+dsa_status_t block_scores_impl(const float* logits, int64_t rows, int64_t width,
+                               int64_t ld_logits, const int32_t* row_ks, const int32_t* row_ke,
+                               int32_t block_size, int32_t row_repeat, int32_t pin_newest,
+                               void* scores, int64_t ld_scores, bool keys, hipStream_t stream) {
   if (rows < 0 || width < 0 || block_size < 1 || row_repeat < 1) return DSA_ERR_INVALID_ARG;
   if (pin_newest != 0 && pin_newest != 1) return DSA_ERR_INVALID_ARG;
   if (ld_logits < width) return DSA_ERR_INVALID_ARG;
@@ -1650,16 +1700,39 @@ dsa_status_t dsa_block_scores(const float* logits, int64_t rows, int64_t width,
   // 13.4 -> 11.7; 64x32768 unchanged at 4.5.
   const int g = lanes_per_block(block_size);
   int64_t ccols = 8192;
-  while (ccols < width && rows * cdiv(width, ccols) > 512) ccols *= 2;
+  while (ccols < width && cdiv(width, ccols) > 512 / rows) ccols *= 2;  // rows * chunks > 512
   int64_t cb = rows >= 1024 ? nblocks : cdiv(ccols, block_size);
   if (g > 0) cb = cdiv(cb, 64 / g) * (64 / g);
   if (cb > nblocks) cb = nblocks;
   const int threads = rows >= 1024 && width < 32768 ? 64 : kThreads;
   p.chunk_blocks = (int32_t)cb;
   p.nchunks = (int32_t)cdiv(nblocks, cb);
-  p.scores = scores;
+  p.scores = static_cast<float*>(scores);
   p.ld_scores = ld_scores;
-  return launch(block_scores_kernel_ptr(g), rows * p.nchunks, threads, 1, 0, stream, p);
+  return launch(keys ? block_keys_kernel_ptr(g) : block_scores_kernel_ptr(g), rows * p.nchunks,
+                threads, 1, 0, stream, p);
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status_t dsa_block_scores(const float* logits, int64_t rows, int64_t width,
+                              int64_t ld_logits, const int32_t* row_ks,
+                              const int32_t* row_ke, int32_t block_size,
+                              int32_t row_repeat, int32_t pin_newest, float* scores,
+                              int64_t ld_scores, hipStream_t stream) {
+  return block_scores_impl(logits, rows, width, ld_logits, row_ks, row_ke, block_size,
+                           row_repeat, pin_newest, scores, ld_scores, false, stream);
+}
+
+dsa_status_t dsa_block_score_keys(const float* logits, int64_t rows, int64_t width,
+                                  int64_t ld_logits, const int32_t* row_ks,
+                                  const int32_t* row_ke, int32_t block_size,
+                                  int32_t row_repeat, int32_t pin_newest, uint32_t* keys,
+                                  int64_t ld_keys, hipStream_t stream) {
+  return block_scores_impl(logits, rows, width, ld_logits, row_ks, row_ke, block_size,
+                           row_repeat, pin_newest, keys, ld_keys, true, stream);
 }
 
 dsa_status_t dsa_select_candidate_blocks_plan(
@@ -1693,6 +1766,7 @@ dsa_status_t dsa_select_candidate_blocks_plan(
   if (!logits || !row_ke) return DSA_ERR_INVALID_ARG;
   if (misaligned(logits, 4) || (scores_out && misaligned(scores_out, 4)))
     return DSA_ERR_INVALID_ARG;
+  if (nblocks > (int64_t)kLdsLimit / 4) return DSA_ERR_UNSUPPORTED;  // keys alone exceed LDS
   const int64_t ww = select_wave_words(nblocks, topk_blocks);
   if (ww * 4 > (int64_t)kLdsLimit) return DSA_ERR_UNSUPPORTED;
 
@@ -1789,11 +1863,18 @@ dsa_status_t dsa_select_candidate_blocks(const float* logits, int64_t rows, int6
                                           0, stream);
 }
 
-dsa_status_t dsa_select_from_scores(const float* scores, int64_t rows, int64_t nscore,
-                                    int64_t ld_scores, int64_t max_global_blocks,
-                                    const int32_t* global_row_ke, int32_t row_repeat,
-                                    int32_t global_block_size, int32_t topk_blocks, int32_t* out,
-                                    int64_t ld_out, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// dsa_select_from_scores / dsa_select_from_keys: `scores` holds fp32 scores
+// or, with keys, their uint32 codes.
+dsa_status_t select_from_scores_impl(const void* scores, int64_t rows, int64_t nscore,
+                                     int64_t ld_scores, int64_t max_global_blocks,
+                                     const int32_t* global_row_ke, int32_t row_repeat,
+                                     int32_t global_block_size, int32_t topk_blocks,
+                                     int32_t* out, int64_t ld_out, bool keys,
+                                     hipStream_t stream) {
   if (rows < 0 || nscore < 0 || max_global_blocks < 0 || row_repeat < 1 ||
       global_block_size < 1 || topk_blocks < 0)
     return DSA_ERR_INVALID_ARG;
@@ -1806,7 +1887,7 @@ dsa_status_t dsa_select_from_scores(const float* scores, int64_t rows, int64_t n
   const int64_t ww = select_wave_words(nblocks, topk_blocks);
   if (ww * 4 > (int64_t)kLdsLimit) return DSA_ERR_UNSUPPORTED;
   Params p = {};
-  p.logits = scores;
+  p.logits = static_cast<const float*>(scores);
   p.rows = rows;
   p.width = nscore;
   p.ld = nscore > 0 ? ld_scores : 1;
@@ -1828,8 +1909,33 @@ dsa_status_t dsa_select_from_scores(const float* scores, int64_t rows, int64_t n
   int64_t waves = cdiv(nblocks, 64);
   const int64_t cap = rows <= 512 ? kWaves : 2;
   if (waves > cap) waves = cap;
-  return launch(reinterpret_cast<void*>(&select_scores_kernel), rows, 64 * (int)waves, 1,
-                (size_t)ww * 4, stream, p);
+  void* fn = keys ? reinterpret_cast<void*>(&select_scores_kernel<true>)
+                 : reinterpret_cast<void*>(&select_scores_kernel<false>);
+  return launch(fn, rows, 64 * (int)waves, 1, (size_t)ww * 4, stream, p);
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status_t dsa_select_from_scores(const float* scores, int64_t rows, int64_t nscore,
+                                    int64_t ld_scores, int64_t max_global_blocks,
+                                    const int32_t* global_row_ke, int32_t row_repeat,
+                                    int32_t global_block_size, int32_t topk_blocks, int32_t* out,
+                                    int64_t ld_out, hipStream_t stream) {
+  return select_from_scores_impl(scores, rows, nscore, ld_scores, max_global_blocks,
+                                 global_row_ke, row_repeat, global_block_size, topk_blocks, out,
+                                 ld_out, false, stream);
+}
+
+dsa_status_t dsa_select_from_keys(const uint32_t* keys, int64_t rows, int64_t nkeys,
+                                  int64_t ld_keys, int64_t max_global_blocks,
+                                  const int32_t* global_row_ke, int32_t row_repeat,
+                                  int32_t global_block_size, int32_t topk_blocks, int32_t* out,
+                                  int64_t ld_out, hipStream_t stream) {
+  return select_from_scores_impl(keys, rows, nkeys, ld_keys, max_global_blocks, global_row_ke,
+                                 row_repeat, global_block_size, topk_blocks, out, ld_out, true,
+                                 stream);
 }
 
 dsa_status_t dsa_mask_candidates(float* logits, int64_t rows, int64_t width, int64_t ld_logits,
@@ -1858,6 +1964,7 @@ dsa_status_t dsa_mask_candidates(float* logits, int64_t rows, int64_t width, int
   m.b_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
   m.vec_ok = !misaligned(logits, 16) && (ld_logits % 4) == 0;
   m.nchunks = cdiv(width, kMaskChunk);
+  if (m.nchunks > INT64_MAX / rows) return DSA_ERR_UNSUPPORTED;  // rows * chunks must fit
   m.items = rows * m.nchunks;
   int64_t grid = m.items < kMaxGrid ? m.items : kMaxGrid;
   void* args[] = {&m};
@@ -1879,6 +1986,7 @@ dsa_status_t dsa_correct_attn_out(const float* out, int64_t B, int64_t H, int64_
   if (B < 0 || H < 0 || D < 0 || N < 0) return DSA_ERR_INVALID_ARG;
   if (B == 0 || H == 0) return DSA_OK;
   if (N < 1 || cp_rank < 0 || cp_rank >= N) return DSA_ERR_INVALID_ARG;
+  if (B > INT32_MAX || H > INT32_MAX) return DSA_ERR_UNSUPPORTED;  // B * H must fit
   if (!lses || !lse_out || misaligned(lses, 4) || misaligned(lse_out, 4))
     return DSA_ERR_INVALID_ARG;
   if (D > 0 && (!out || !new_out || misaligned(out, 4) || misaligned(new_out, 4)))

@@ -134,13 +134,13 @@ def test_auto_plan_without_workspace_takes_the_group_plan():
         assert _sel(**shape, **ws, plan=4) == 3
 
 
-def _bs(**kw):
+def _bs(keys=False, **kw):
     a = dict(logits=FAKE, rows=4, width=64, ld=64, ks=None, ke=FAKE, B=8, R=1, pin=1,
              scores=FAKE2, ld_scores=8)
     a.update(kw)
-    return B.lib().dsa_block_scores(a["logits"], a["rows"], a["width"], a["ld"], a["ks"],
-                                    a["ke"], a["B"], a["R"], a["pin"], a["scores"],
-                                    a["ld_scores"], None)
+    fn = B.lib().dsa_block_score_keys if keys else B.lib().dsa_block_scores
+    return fn(a["logits"], a["rows"], a["width"], a["ld"], a["ks"], a["ke"], a["B"], a["R"],
+              a["pin"], a["scores"], a["ld_scores"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -151,6 +151,7 @@ def _bs(**kw):
 ])
 def test_block_scores_rejects_on_host(kw, code):
     assert _bs(**kw) == code
+    assert _bs(keys=True, **kw) == code   # the uint32-code variant checks alike
 
 
 def test_calib_rejects_on_host():
@@ -180,11 +181,12 @@ def test_binding_refuses_cpu_tensors():
 
 # --- the entry points after selection: host-side argument checks (no launch)
 
-def _sfs(**kw):
+def _sfs(keys=False, **kw):
     a = dict(scores=FAKE, rows=4, nscore=8, ld=8, mgb=8, ke=FAKE, R=1, G=4, k=4, out=FAKE2, ld_out=4)
     a.update(kw)
-    return B.lib().dsa_select_from_scores(a["scores"], a["rows"], a["nscore"], a["ld"], a["mgb"],
-                                          a["ke"], a["R"], a["G"], a["k"], a["out"], a["ld_out"], None)
+    fn = B.lib().dsa_select_from_keys if keys else B.lib().dsa_select_from_scores
+    return fn(a["scores"], a["rows"], a["nscore"], a["ld"], a["mgb"], a["ke"], a["R"], a["G"],
+              a["k"], a["out"], a["ld_out"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -196,6 +198,7 @@ def _sfs(**kw):
 ])
 def test_select_from_scores_rejects_on_host(kw, code):
     assert _sfs(**kw) == code
+    assert _sfs(keys=True, **kw) == code   # the uint32-code variant checks alike
 
 
 def _mask(**kw):

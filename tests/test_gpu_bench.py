@@ -20,7 +20,8 @@ def _run(*args):
 
 
 @pytest.mark.parametrize("args", [("--config", "1", "--per-config", "none"), ("--op", "lse"),
-                                  ("--op", "blockscores")])
+                                  ("--op", "blockscores"), ("--op", "blockscores", "--keys"),
+                                  ("--op", "scores", "--keys")])
 def test_bench_line(args):
     d = _run(*args, "--steps", "20", "--warmup", "5", "--cpu-seconds", "0.5",
              "--rotate-bytes", "0.25")

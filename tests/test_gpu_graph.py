@@ -113,3 +113,82 @@ def test_mask_and_lse_in_graph():
         lse.fill_(777.0)
 
     _check_replays(run, [x, new, lse], clear)
+
+
+def test_block_score_keys_and_select_from_keys_in_graph():
+    w = workloads.config(2)
+    x = torch.from_numpy(w.logits).to(DEV)
+    ke = _i32(w.row_ke)
+    nb = -(-w.width // w.block_size)
+    codes = torch.empty((w.rows, nb), dtype=torch.int32, device=DEV)
+    out = torch.empty((w.rows, w.topk_blocks), dtype=torch.int32, device=DEV)
+
+    def run():
+        dsa.block_score_keys(x, None, ke, w.block_size, w.row_repeat, pin_newest=False, out=codes)
+        dsa.select_from_keys(codes, ke, w.topk_blocks, w.block_size, nb, out, w.row_repeat)
+
+    def clear():
+        codes.fill_(12345)
+        out.fill_(12345)
+
+    _check_replays(run, [codes, out], clear)
+
+
+def test_workspace_is_not_allocated_under_capture():
+    """A call whose plan needs a workspace, captured on a stream that has
+    none yet, raises instead of allocating inside the capture."""
+    w = workloads.config(2)
+    x = torch.from_numpy(w.logits).to(DEV)
+    ke = _i32(w.row_ke)
+    out = torch.empty((w.rows, w.topk_blocks), dtype=torch.int32, device=DEV)
+    side = torch.cuda.Stream(DEV)
+    graph = torch.cuda.CUDAGraph()
+    with pytest.raises(RuntimeError, match="captured"):
+        with torch.cuda.graph(graph, stream=side):
+            dsa.select_candidate_blocks(x, None, ke, w.topk_blocks, w.block_size, out,
+                                        w.row_repeat, plan=4)
+    torch.cuda.synchronize()
+
+
+def test_graph_keeps_its_workspace_after_growth():
+    """A graph captured with a workspace keeps replaying correctly after an
+    eager call has grown that workspace: the replaced buffer stays alive."""
+    small, big = workloads.config(2), workloads.config(4)
+    xs, xb = torch.from_numpy(small.logits).to(DEV), torch.from_numpy(big.logits).to(DEV)
+    ke_s, ke_b = _i32(small.row_ke), _i32(big.row_ke)
+    ws = dsa.Workspace(DEV, dsa.select_workspace_bytes(small.rows, small.width, small.block_size,
+                                                       small.topk_blocks))
+    out = torch.empty((small.rows, small.topk_blocks), dtype=torch.int32, device=DEV)
+    out_b = torch.empty((big.rows, big.topk_blocks), dtype=torch.int32, device=DEV)
+
+    def run():
+        dsa.select_candidate_blocks(xs, None, ke_s, small.topk_blocks, small.block_size, out,
+                                    small.row_repeat, workspace=ws, plan=4)
+
+    run()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    side = torch.cuda.Stream(DEV)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        run()
+    old = ws.buf.data_ptr()
+    dsa.select_candidate_blocks(xb, None, ke_b, big.topk_blocks, big.block_size, out_b,
+                                big.row_repeat, workspace=ws, plan=4)   # grows the workspace
+    torch.cuda.synchronize()
+    assert ws.buf.data_ptr() != old
+    big_ref = out_b.clone()
+    for _ in range(3):
+        out.fill_(12345)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        dsa.select_candidate_blocks(xb, None, ke_b, big.topk_blocks, big.block_size, out_b,
+                                    big.row_repeat, workspace=ws, plan=4)
+        torch.cuda.synchronize()
+        assert torch.equal(out_b, big_ref)

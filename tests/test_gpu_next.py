@@ -6,6 +6,10 @@
   plus the DCP decomposition run on the GPU (shards scored by
   dsa_block_scores with the pin off, reduced with an element-wise maximum)
   against the unsharded GPU selection.
+- dsa_block_score_keys / dsa_select_from_keys (the same DCP steps on
+  order-preserving uint32 codes): codes bit-exact on random cases and at
+  full size, the selection on random and raw codes, and the DCP
+  decomposition reduced by an integer maximum with +-0 and NaN present.
 - dsa_mask_candidates: bit-exact against the oracle on random cases (odd
   widths and block sizes, unaligned rows, negative starts) and on the
   prefill chunk masked with its own selection (every row).
@@ -106,8 +110,8 @@ def test_select_from_scores_row_counts(rows, k):
 def test_dcp_decomposition_on_gpu(W):
     rng = np.random.default_rng(40 + W)
     rows, width, B, k = 24, 20000, 64, 32
-    x = (rng.standard_normal((rows, width)) + 0.125).astype(np.float32)
-    x[x == 0] = 1.0                                      # no signed zeros in the reduce
+    x = (np.rint(rng.standard_normal((rows, width)) * 4) / 4).astype(np.float32)
+    x[rng.random((rows, width)) < 0.2] *= -0.0            # +0 and -0 side by side
     x[rng.random((rows, width)) < 1e-4] = np.nan
     ends = rng.integers(0, width + 1, size=rows).astype(np.int32)
     ends[0] = 0
@@ -119,7 +123,9 @@ def test_dcp_decomposition_on_gpu(W):
         lend = np.maximum(0, -(-(ends.astype(np.int64) - wr) // W)).astype(np.int32)
         sc = dsa.block_scores(local, None, _i32(lend), B // W, 1, pin_newest=False)
         n = min(sc.shape[1], nblocks)
-        reduced[:, :n] = torch.maximum(reduced[:, :n], sc[:, :n])   # NaN propagates
+        # torch.maximum propagates NaN; which zero it keeps for -0 vs +0 is
+        # not specified, but the ranking treats them alike (ids compared only)
+        reduced[:, :n] = torch.maximum(reduced[:, :n], sc[:, :n])
     got = torch.empty((rows, k), dtype=torch.int32, device=DEV)
     dsa.select_from_scores(reduced, _i32(ends), k, B, nblocks, got)
     ref = torch.empty((rows, k), dtype=torch.int32, device=DEV)
@@ -147,6 +153,111 @@ def test_dcp_local_scores_full_size():
     last = -(-(w.row_ke.astype(np.int64) - w.row_ks) // w.block_size)   # blocks with a column
     col = np.arange(nb)[None, :]
     assert np.all(np.isneginf(got[col >= last[:, None]]))
+
+
+# --------------------------------------------- uint32 score codes (DCP reduce)
+
+_SIGN = -2 ** 31
+
+
+def _codes_max(a: torch.Tensor, b: torch.Tensor) -> torch.Tensor:
+    """Unsigned maximum of two code tensors held as int32 bit patterns:
+    flipping the sign bit makes signed order the codes' unsigned order."""
+    return torch.maximum(a ^ _SIGN, b ^ _SIGN) ^ _SIGN
+
+
+def _np_codes(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int32).cpu().numpy().view(np.uint32)
+
+
+@pytest.mark.parametrize("pin", [True, False])
+def test_block_score_keys_random(pin):
+    for i in range(60):
+        w = workloads.random_case(700 + i, max_rows=9, max_width=3000, max_block=300,
+                                  special=i % 2 == 0)
+        x = torch.from_numpy(w.logits).to(DEV)
+        ks = None if w.row_ks is None else _i32(w.row_ks)
+        got = dsa.block_score_keys(x, ks, _i32(w.row_ke), w.block_size, w.row_repeat,
+                                   pin_newest=pin)
+        torch.cuda.synchronize()
+        exp = oracle.block_score_keys(w.logits, w.row_ks, w.row_ke, w.block_size, w.row_repeat,
+                                      pin_newest=pin)
+        assert np.array_equal(_np_codes(got), exp), i
+
+
+def test_block_score_keys_full_size():
+    """One DCP rank's local scores at the benchmarked size as codes: every
+    code of every row equals the oracle's."""
+    w = workloads.dcp_local_logits()
+    x = torch.from_numpy(w.logits).to(DEV)
+    got = dsa.block_score_keys(x, _i32(w.row_ks), _i32(w.row_ke), w.block_size, 1,
+                               pin_newest=False)
+    exp = oracle.block_score_keys(w.logits, w.row_ks, w.row_ke, w.block_size, 1,
+                                  pin_newest=False, nthreads=HOST_THREADS)
+    assert np.array_equal(_np_codes(got), exp)
+
+
+def test_select_from_keys_random_cases():
+    """Codes of the random DCP score cases, and raw uint32 codes of every
+    range (the codes of NaNs with other payloads and signs included)."""
+    for seed in range(60):
+        w = workloads.random_scores_case(seed)
+        rows = w.scores.shape[0]
+        codes = oracle.score_keys(w.scores)
+        if seed % 3 == 2 and codes.size:   # any uint32 at all in a third of the cells
+            g = np.random.default_rng(seed)
+            pick = g.random(codes.shape) < 0.3
+            codes[pick] = g.integers(0, 2 ** 32, size=int(pick.sum()), dtype=np.uint64)
+        exp = np.empty((rows, w.topk_blocks), np.int32)
+        oracle.select_from_keys(codes, w.global_row_ke, w.topk_blocks, w.global_block_size,
+                                w.max_global_blocks, exp, w.row_repeat)
+        kd = torch.from_numpy(codes.view(np.int32)).to(DEV)
+        out = torch.full((rows, w.topk_blocks), 777, dtype=torch.int32, device=DEV)
+        dsa.select_from_keys(kd, _i32(w.global_row_ke), w.topk_blocks, w.global_block_size,
+                             w.max_global_blocks, out, w.row_repeat)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), exp), seed
+
+
+@pytest.mark.parametrize("W", [2, 4, 8])
+def test_dcp_decomposition_keys_on_gpu(W):
+    """The page's DCP branch on one GPU with exact integer codes: each of W
+    shards (token t on shard t mod W) scored by dsa_block_score_keys at
+    block size B/W with the pin off, reduced by an unsigned maximum, equals
+    the oracle's codes of the unsharded pin-off scores bit for bit (+0 and
+    -0 side by side, NaN), and dsa_select_from_keys then gives the oracle's
+    unsharded selection."""
+    rng = np.random.default_rng(80 + W)
+    rows, width, B, k = 24, 20000, 64, 32
+    x = (np.rint(rng.standard_normal((rows, width)) * 4) / 4).astype(np.float32)
+    x[rng.random((rows, width)) < 0.3] *= -0.0
+    x[rng.random((rows, width)) < 1e-4] = np.nan
+    x[5, :] = -0.0
+    x[6, 128:192] = 0.0
+    x[6, 150] = -0.0
+    ends = rng.integers(0, width + 1, size=rows).astype(np.int32)
+    ends[0] = 0
+    ends[5] = ends[6] = width
+    xd = torch.from_numpy(x).to(DEV)
+    nblocks = -(-width // B)
+    red = torch.full((rows, nblocks), oracle.score_key(float("-inf")), dtype=torch.int32,
+                     device=DEV)                      # the code of -inf, 0x007FFFFF
+    for wr in range(W):
+        local = xd[:, wr::W].contiguous()
+        lend = np.maximum(0, -(-(ends.astype(np.int64) - wr) // W)).astype(np.int32)
+        kc = dsa.block_score_keys(local, None, _i32(lend), B // W, 1, pin_newest=False)
+        n = min(kc.shape[1], nblocks)
+        red[:, :n] = _codes_max(red[:, :n], kc.view(torch.int32)[:, :n])
+    got_codes = _np_codes(red)
+    exp_codes = oracle.block_score_keys(x, None, ends, B, 1, pin_newest=False)
+    assert np.array_equal(got_codes, exp_codes)
+    assert got_codes[5, 0] == oracle.score_key(-0.0) and got_codes[6, 2] == oracle.score_key(0.0)
+    got = torch.empty((rows, k), dtype=torch.int32, device=DEV)
+    dsa.select_from_keys(red, _i32(ends), k, B, nblocks, got)
+    torch.cuda.synchronize()
+    exp = np.empty((rows, k), np.int32)
+    oracle.select_candidate_blocks(x, None, ends, k, B, exp)
+    assert np.array_equal(got.cpu().numpy(), exp)
 
 
 # ------------------------------------------------------------------- masking
