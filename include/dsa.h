@@ -166,6 +166,41 @@ dsa_status_t dsa_select_candidate_blocks(const float* logits, int64_t rows, int6
                                          int64_t ld_scores, void* workspace,
                                          size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of the static device scratch of dsa_select_candidate_blocks_noalloc
+ * (per GPU, held until the process ends). */
+#define DSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * dsa_select_candidate_blocks for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no workspace argument.  The split and pair plans use instead a
+ * static device array of DSA_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends; this call allocates nothing
+ * (no hipMalloc, no allocating library routine).  Its first call on a device
+ * takes the array's address there (hipGetSymbolAddress) and enqueues a small
+ * kernel on `stream` that clears the pair plan's arrival counters; calls
+ * that complete leave them zero.
+ *
+ * Results are those of dsa_select_candidate_blocks (the same automatic plan).
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (other streams, other threads) race and must not be issued
+ * concurrently; calls on different GPUs are independent.
+ *
+ * DSA_ERR_WORKSPACE: the automatic plan of this shape needs more scratch
+ *   than DSA_NOALLOC_SCRATCH_BYTES (dsa_select_workspace_bytes(...) bytes);
+ *   nothing is written.  Shapes whose plan needs no scratch always run.
+ * DSA_ERR_HIP: also when the device or the array's address cannot be
+ *   obtained.  Other arguments, early exits and errors as
+ *   dsa_select_candidate_blocks.
+ */
+dsa_status_t dsa_select_candidate_blocks_noalloc(const float* logits, int64_t rows,
+                                                 int64_t width, int64_t ld_logits,
+                                                 const int32_t* row_ks, const int32_t* row_ke,
+                                                 int32_t topk_blocks, int32_t block_size,
+                                                 int32_t row_repeat, int32_t* out, int64_t ld_out,
+                                                 float* scores_out, int64_t ld_scores,
+                                                 hipStream_t stream);
+
 /*
  * dsa_select_candidate_blocks with an explicit launch plan, for tests and
  * tuning.  Results are identical for every plan.

@@ -5,6 +5,7 @@ include/dsa.h); this package is its Python binding.  Build the library with
 ``python -m sparse_attention_kv_dsa_amd.build``.
 
     select_candidate_blocks(logits, row_ks, row_ke, topk_blocks, block_size, out, row_repeat=1)
+    select_candidate_blocks_noalloc(...)    # the same with no workspace and no allocation
     block_scores(logits, row_ks, row_ke, block_size, row_repeat=1, pin_newest=True)
     block_score_keys(...)                   # the same scores as order-preserving uint32 codes
     select_from_scores(scores, global_row_ke, topk_blocks, global_block_size,
@@ -22,6 +23,7 @@ from ._binding import (  # noqa: F401
     lib,
     mask_candidates,
     select_candidate_blocks,
+    select_candidate_blocks_noalloc,
     select_from_keys,
     select_from_scores,
     select_plan,

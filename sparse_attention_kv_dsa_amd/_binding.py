@@ -51,6 +51,9 @@ def lib() -> ctypes.CDLL:
                                                                i32, vp, i64, vp, i64, vp, sz, i32,
                                                                i32, vp]
                 L.dsa_select_candidate_blocks_plan.restype = ctypes.c_int
+                L.dsa_select_candidate_blocks_noalloc.argtypes = [vp, i64, i64, i64, vp, vp, i32,
+                                                                  i32, i32, vp, i64, vp, i64, vp]
+                L.dsa_select_candidate_blocks_noalloc.restype = ctypes.c_int
                 L.dsa_select_plan.argtypes = [i64, i64, i32, i32, ctypes.POINTER(i32),
                                               ctypes.POINTER(i32)]
                 L.dsa_select_plan.restype = ctypes.c_int
@@ -270,6 +273,31 @@ def select_candidate_blocks(logits: torch.Tensor, row_ks: torch.Tensor | None,
         _ptr(out), _ld(out), _ptr(scores_out), ld_scores, ws_ptr, ws_bytes, plan, plan_arg,
         stream)
     _raise(code, "dsa_select_candidate_blocks")
+
+
+def select_candidate_blocks_noalloc(logits: torch.Tensor, row_ks: torch.Tensor | None,
+                                    row_ke: torch.Tensor, topk_blocks: int, block_size: int,
+                                    out: torch.Tensor, row_repeat: int = 1, *,
+                                    scores_out: torch.Tensor | None = None) -> None:
+    """select_candidate_blocks with no workspace and no allocation
+    (dsa_select_candidate_blocks_noalloc): plans that need scratch use the
+    library's static per-GPU array, so calls on one GPU must not overlap."""
+    ld = _check_logits(logits)
+    rows, width = logits.shape
+    if out.dtype != torch.int32 or out.device != logits.device or out.shape[0] != rows:
+        raise ValueError("out must be int32 [rows, >= topk_blocks] on the logits' device")
+    groups = -(-rows // row_repeat) if row_repeat > 0 else 0
+    ks = _bounds(row_ks, "row_ks", groups, logits.device)
+    ke = _bounds(row_ke, "row_ke", groups, logits.device)
+    ld_scores = 0
+    if scores_out is not None:
+        if scores_out.dtype != torch.float32 or scores_out.device != logits.device:
+            raise ValueError("scores_out must be float32 on the logits' device")
+        ld_scores = _ld(scores_out)
+    code = lib().dsa_select_candidate_blocks_noalloc(
+        _ptr(logits), rows, width, ld, _ptr(ks), _ptr(ke), topk_blocks, block_size, row_repeat,
+        _ptr(out), _ld(out), _ptr(scores_out), ld_scores, _stream(logits.device))
+    _raise(code, "dsa_select_candidate_blocks_noalloc")
 
 
 def select_from_scores(scores: torch.Tensor, global_row_ke: torch.Tensor, topk_blocks: int,

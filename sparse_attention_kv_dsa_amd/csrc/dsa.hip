@@ -45,6 +45,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "dsa.h"
 #include "stream_geom.h"
 
@@ -1428,6 +1430,12 @@ __global__ void __launch_bounds__(kThreads) correct_attn_out_kernel(LseParams q)
   }
 }
 
+__global__ void __launch_bounds__(kThreads) clear_words_kernel(uint32_t* p, int32_t n) {
+  for (int32_t i = (int32_t)(blockIdx.x * kThreads + threadIdx.x); i < n;
+       i += (int32_t)(gridDim.x * kThreads))
+    p[i] = 0u;
+}
+
 __global__ void __launch_bounds__(kThreads) fill_minus_one_kernel(int32_t* out, int64_t rows,
                                                                   int64_t ld, int32_t k) {
   const int64_t n = rows * k;
@@ -1592,6 +1600,46 @@ void pair_shape(int64_t rows, int64_t width, int* parts, int* waves) {
   const int64_t by_width = width / 8192 > 2 ? width / 8192 : 2;
   *parts = (int)(n < by_width ? n : by_width);
   *waves = width >= 262144 ? 16 : 8;
+}
+
+// ---------------------------------------------------- static scratch --
+//
+// dsa_select_candidate_blocks_noalloc's workspace: a file-scope device array
+// that every GPU the library runs on holds once, until the process ends.
+// Host code never uses the array's name as an address (on the host it is a
+// stand-in, not device memory): the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// kept per device.  The first kCountBytes are the pair plan's arrival
+// counters, cleared when the address is taken (and zero-initialised at
+// load); every completed call leaves them zero.
+static __device__ __align__(256) unsigned char scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address, set up on its first use (the clear
+// of the counters is enqueued on `stream`, ahead of the caller's work).
+dsa_status_t device_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return DSA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return DSA_ERR_HIP;
+    }
+    clear_words_kernel<<<dim3(2), dim3(kThreads), 0, stream>>>(static_cast<uint32_t*>(ptr),
+                                                                (int32_t)(kCountBytes / 4));
+    if (hipGetLastError() != hipSuccess) return DSA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
 }
 
 }  // namespace
@@ -1861,6 +1909,34 @@ dsa_status_t dsa_select_candidate_blocks(const float* logits, int64_t rows, int6
                                           topk_blocks, block_size, row_repeat, out, ld_out,
                                           scores_out, ld_scores, workspace, workspace_bytes, 0,
                                           0, stream);
+}
+
+dsa_status_t dsa_select_candidate_blocks_noalloc(const float* logits, int64_t rows,
+                                                 int64_t width, int64_t ld_logits,
+                                                 const int32_t* row_ks, const int32_t* row_ke,
+                                                 int32_t topk_blocks, int32_t block_size,
+                                                 int32_t row_repeat, int32_t* out, int64_t ld_out,
+                                                 float* scores_out, int64_t ld_scores,
+                                                 hipStream_t stream) {
+  if (rows < 0 || width < 0 || block_size < 1 || row_repeat < 1 || topk_blocks < 0)
+    return DSA_ERR_INVALID_ARG;
+  int32_t plan = 0, plan_arg = 0;
+  dsa_select_plan(rows, width, block_size, topk_blocks, &plan, &plan_arg);
+  void* ws = nullptr;
+  if (plan == kPlanSplit || plan == kPlanPair) {
+    if (dsa_select_workspace_bytes(rows, width, block_size, topk_blocks) >
+        (size_t)DSA_NOALLOC_SCRATCH_BYTES)
+      return DSA_ERR_WORKSPACE;  // this shape's plan needs more than the static scratch
+    if (rows > 0 && width > 0 && topk_blocks > 0) {
+      const dsa_status_t st = device_scratch(stream, &ws);
+      if (st != DSA_OK) return st;
+    }
+  }
+  return dsa_select_candidate_blocks_plan(logits, rows, width, ld_logits, row_ks, row_ke,
+                                          topk_blocks, block_size, row_repeat, out, ld_out,
+                                          scores_out, ld_scores, ws,
+                                          ws ? (size_t)DSA_NOALLOC_SCRATCH_BYTES : 0, plan,
+                                          plan_arg, stream);
 }
 
 }  // extern "C"

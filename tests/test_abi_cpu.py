@@ -237,3 +237,24 @@ def _lse(**kw):
 ])
 def test_correct_attn_out_rejects_on_host(kw, code):
     assert _lse(**kw) == code
+
+
+def test_noalloc_host_checks():
+    """dsa_select_candidate_blocks_noalloc rejects on the host, before any
+    device call: invalid arguments, and a shape whose plan needs more than
+    its static scratch (16 MiB).  With no GPU visible, a shape that passes
+    fails at the device query (DSA_ERR_HIP) without touching memory."""
+    import torch
+    L = B.lib()
+
+    def call(rows, width, B_, k, ld=None, ke=FAKE, out=FAKE2):
+        return L.dsa_select_candidate_blocks_noalloc(FAKE, rows, width, ld or width, None, ke, k,
+                                                     B_, 1, out, k, None, 0, None)
+
+    assert B.select_workspace_bytes(300, 448000, 32, 16) > 16 << 20
+    assert call(300, 448000, 32, 16) == 3            # the split plan's keys exceed the scratch
+    assert call(-1, 100, 8, 4) == 1 and call(4, 100, 0, 4) == 1 and call(4, 100, 8, -1) == 1
+    assert call(4, 100, 8, 4, ld=99) == 1 and call(4, 100, 8, 4, ke=None) == 1
+    assert call(0, 100, 8, 4) == 0 and call(4, 100, 8, 0) == 0   # nothing to do
+    if torch.cuda.device_count() == 0:
+        assert call(64, 32768, 64, 32) == 4           # pair plan: no device to hold the scratch
