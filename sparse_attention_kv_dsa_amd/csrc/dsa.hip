@@ -756,17 +756,18 @@ constexpr int kBoundGroups128 = 2;  // 32 < k <= 64
 // from bound_radix for larger k.  Same-address LDS max serialises per lane
 // on this chip, so the maxima and the bound go through per-wave LDS rows
 // and slots, not atomics.
-template <bool WG, int BOUND, bool KC>
+template <bool WG, int BOUND, bool KC, bool PRE = false>
 __device__ __forceinline__ void select_row_general(const Params& p, const RowGeom& g,
                                                    uint32_t* keys, uint32_t* ctl, uint32_t* area,
-                                                   int32_t* out_row, int wave, int nw) {
+                                                   int32_t* out_row, int wave, int nw,
+                                                   const LaneKeys& pre) {
   const int lane = threadIdx.x & 63;
   const int tid = wave * 64 + lane;
   const int nt = nw * 64;
   const int32_t nsel = g.nsel, k = p.k;
   uint64_t* cand = reinterpret_cast<uint64_t*>(area);
   uint32_t t0, nvalid;
-  const LaneKeys lk = lane_keys<KC>(keys, g, wave, nt);
+  const LaneKeys lk = PRE ? pre : lane_keys<KC>(keys, g, wave, nt);
 
   if constexpr (BOUND == kBoundRadix) {
     bound_radix<WG>(g, k, keys, lk, ctl, area, wave, nw);
@@ -812,12 +813,30 @@ __device__ __forceinline__ void select_row_general(const Params& p, const RowGeo
         }
       }
       const uint32_t kq = (uint32_t)k < nvalid ? (uint32_t)k : nvalid;
-      uint32_t t = 0u;
-      for (int bit = 31; bit >= 0; --bit) {
+      // Any t with at least kq maxima >= t bounds the keff-th key from
+      // below; the exact kq-th maximum only trims candidates.  So the search
+      // stops after the top 16 bits unless more than kq + kq/4 maxima lie at
+      // or above t (maxima packed within 2^16 codes of each other, where the
+      // lower bits still separate them).  Each step is a dependent chain of
+      // two ballots and scalar arithmetic in one wave.
+      uint32_t t = 0u, ct = 128u;  // ct: maxima >= t (all 128 for t = 0)
+#pragma unroll
+      for (int bit = 31; bit >= 16; --bit) {
         const uint32_t c = t | (1u << bit);
         const uint32_t cnt =
             (uint32_t)__popcll(__ballot(g0 >= c)) + (uint32_t)__popcll(__ballot(g1 >= c));
-        if (cnt >= kq) t = c;
+        if (cnt >= kq) {
+          t = c;
+          ct = cnt;
+        }
+      }
+      if (ct > kq + (kq >> 2)) {  // wave-uniform
+        for (int bit = 15; bit >= 0; --bit) {
+          const uint32_t c = t | (1u << bit);
+          const uint32_t cnt =
+              (uint32_t)__popcll(__ballot(g0 >= c)) + (uint32_t)__popcll(__ballot(g1 >= c));
+          if (cnt >= kq) t = c;
+        }
       }
       if (lane == 0) ctl[kCtlT0] = t;
     }
@@ -863,24 +882,26 @@ __device__ __forceinline__ void select_row_general(const Params& p, const RowGeo
   {
     const uint32_t tt = t0 > 1u ? t0 : 1u;
     if (KC && lk.cached) {
-      // every ballot first, then one atomic reserves all of this wave's slots
-      uint64_t m[kKeyRegs];
+      // every ballot first, then one atomic reserves all of this wave's
+      // slots.  Keys past the lane's count are 0, below tt >= 1.
       uint32_t tot = 0u;
 #pragma unroll
-      for (int j = 0; j < kKeyRegs; ++j) {
-        m[j] = __ballot(j < lk.nj && lk.v[j] >= tt);
-        tot += (uint32_t)__popcll(m[j]);
-      }
+      for (int j = 0; j < kKeyRegs; ++j) tot += (uint32_t)__popcll(__ballot(lk.v[j] >= tt));
       if (tot != 0u) {  // wave-uniform
         uint32_t b0 = 0u;
         if (lane == 0) b0 = atomicAdd(&ctl[kCtlCand], tot);
         uint32_t pos = (uint32_t)__builtin_amdgcn_readlane((int)b0, 0);
+        const bool fits = pos + tot <= (uint32_t)kCandCap;  // else only the in-range slots
+        uint32_t id0 = ~(uint32_t)(wave * 64 + lane);
+        asm volatile("" : "+v"(id0));  // not hoisted out of the row loop (8 live VGPRs)
 #pragma unroll
         for (int j = 0; j < kKeyRegs; ++j) {
-          const uint32_t at = pos + lanes_below(m[j]);
-          if (((m[j] >> lane) & 1ull) && at < (uint32_t)kCandCap)
-            cand[at] = cand_word(lk.v[j], (uint32_t)(wave * 64 + j * nt + lane));
-          pos += (uint32_t)__popcll(m[j]);
+          const bool c = lk.v[j] >= tt;
+          const uint64_t m = __ballot(c);
+          const uint32_t at = pos + lanes_below(m);
+          if (c && (fits || at < (uint32_t)kCandCap))
+            cand[at] = ((uint64_t)lk.v[j] << 32) | (uint64_t)(id0 - (uint32_t)(j * nt));
+          pos += (uint32_t)__popcll(m);
         }
       }
     } else {
@@ -906,7 +927,16 @@ __device__ __forceinline__ void select_row_general(const Params& p, const RowGeo
   if (ncand <= kCandCap) {
     rank_candidates(cand, ncand, keff, out_row, wave, nw);
     for (int32_t j = keff + tid; j < k; j += nt) out_row[j] = -1;
-  } else if (wave == 0) {
+  } else {
+    if constexpr (PRE) {  // the exact select reads the keys from LDS
+#pragma unroll
+      for (int j = 0; j < kKeyRegs; ++j) {
+        const int32_t i = wave * 64 + j * nt + lane;
+        if (j < lk.nj && i < nsel) keys[i] = lk.v[j];
+      }
+      row_barrier<WG>();
+    }
+    if (wave != 0) return;
     for (int32_t b = g.nvb + lane; b < nsel; b += 64) keys[b] = kKeyNegInf;
     wave_sync();
     if (g.pin >= 0 && lane == 0) keys[g.pin] = kKeyPosInf;
@@ -921,17 +951,17 @@ __device__ __forceinline__ void select_row_general(const Params& p, const RowGeo
 // (16-byte aligned, max(kAreaMinWords, 2*kcap) words) are this row's LDS
 // scratch, cleared by select_row_prepare before the caller's last barrier.
 // Also writes the optional fp32 score row.
-template <bool WG, bool KC = false>
+template <bool WG, bool KC = false, int FB = -1, bool PRE = false>
 __device__ __forceinline__ void select_row(const Params& p, int64_t r, const RowGeom& g,
                                            uint32_t* keys, uint32_t* ctl, uint32_t* area,
-                                           int wave, int nw) {
+                                           int wave, int nw, const LaneKeys& pre = LaneKeys{}) {
   const int lane = threadIdx.x & 63;
   const int tid = wave * 64 + lane;
   const int nt = nw * 64;
   const int32_t nsel = g.nsel, k = p.k;
   int32_t* out_row = p.out + r * p.ld_out;
 
-  if (p.scores) {
+  if (!PRE && p.scores) {
     float* srow = p.scores + r * p.ld_scores;
     for (int32_t b = tid; b < p.nblocks; b += nt)
       srow[b] = b < nsel ? key_value(block_key(keys, g, b)) : -__builtin_inff();
@@ -941,7 +971,7 @@ __device__ __forceinline__ void select_row(const Params& p, int64_t r, const Row
     // One candidate per lane of wave 0: rank them all directly.
     if (wave == 0) {
       uint64_t* cand = reinterpret_cast<uint64_t*>(area);
-      const uint32_t rk = select_rank_key(keys, g, lane);
+      const uint32_t rk = PRE ? pre.v[0] : select_rank_key(keys, g, lane);
       const int32_t nvalid = (int32_t)__popcll(__ballot(rk != 0u));
       const int32_t keff = k < nvalid ? k : nvalid;
       cand[lane] = cand_word(rk, (uint32_t)lane);
@@ -951,12 +981,16 @@ __device__ __forceinline__ void select_row(const Params& p, int64_t r, const Row
     }
     return;
   }
-  if (k <= 32)
-    select_row_general<WG, kBoundGroups64, KC>(p, g, keys, ctl, area, out_row, wave, nw);
-  else if (k <= 64 && ((nw & 1) == 0 || nw <= 8))
-    select_row_general<WG, kBoundGroups128, KC>(p, g, keys, ctl, area, out_row, wave, nw);
-  else
-    select_row_general<WG, kBoundRadix, KC>(p, g, keys, ctl, area, out_row, wave, nw);
+  if constexpr (FB >= 0) {
+    select_row_general<WG, FB, KC, PRE>(p, g, keys, ctl, area, out_row, wave, nw, pre);
+  } else {
+    if (k <= 32)
+      select_row_general<WG, kBoundGroups64, KC, PRE>(p, g, keys, ctl, area, out_row, wave, nw, pre);
+    else if (k <= 64 && ((nw & 1) == 0 || nw <= 8))
+      select_row_general<WG, kBoundGroups128, KC, PRE>(p, g, keys, ctl, area, out_row, wave, nw, pre);
+    else
+      select_row_general<WG, kBoundRadix, KC, PRE>(p, g, keys, ctl, area, out_row, wave, nw, pre);
+  }
 }
 
 // Plan "wave": one wave per row, blockDim/64 rows per workgroup, no barrier.
@@ -1189,16 +1223,24 @@ block_scores_kernel(Params p) {
 // B = global block size, nblocks = max(max_global_blocks, 1).  Columns past
 // min(width, nblocks) are -inf; the pin is floor((e-1)/B) clamped to the
 // last block; rows with e <= 0 select nothing.
+// FB: the candidate bound, fixed at compile time (the host knows k and the
+// wave count), so each instance holds one bound's code.  PRE: every row has
+// at most kKeyRegs keys per lane; the lanes load their keys straight into
+// registers (all loads in flight at once) and the select works from there,
+// with no LDS copy of the row unless it takes the exact fallback.
 // Seven waves per SIMD (at most 72 VGPRs, no spills): rows' selects share
 // each CU.  On 8192 rows of 1024 scores at k = 64 this took 36.3 -> 31.1 us
 // against the compiler's own choice (83 VGPRs, five waves); six waves gave
-// 32.4, eight spill to scratch and gave 32.0.
-template <bool KEYS>
+// 32.4, eight spill to scratch and gave 32.0 (measured before FB and PRE;
+// with them six and eight waves are still slower).
+template <bool KEYS, int FB, bool PRE>
 __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7)))
 select_scores_kernel(Params p) {
   extern __shared__ uint32_t smem[];
   const int wave = wave_index();
+  const int lane = threadIdx.x & 63;
   const int nw = blockDim.x >> 6;
+  const int32_t nt = (int32_t)blockDim.x;
   uint32_t* ctl = smem + p.keys_words;
   uint32_t* area = ctl + kCtlWords;
   const int32_t ncopy = p.width < p.nblocks ? (int32_t)p.width : p.nblocks;
@@ -1217,29 +1259,59 @@ select_scores_kernel(Params p) {
       g.pin = (int32_t)(q < p.nblocks - 1 ? q : p.nblocks - 1);
     }
     g.nsel = g.nvb > g.pin + 1 ? g.nvb : g.pin + 1;
-    select_row_prepare(ctl, area, threadIdx.x, blockDim.x);
-    const int32_t nt = (int32_t)blockDim.x;
-    for (int32_t b0 = 0; b0 < g.nvb; b0 += 4 * nt) {  // four loads in flight per lane
-      uint32_t v[4];
+    if constexpr (PRE) {
+      // key i = wave*64 + j*nt + lane, the order lane_keys uses
+      const int32_t first = wave * 64;
+      const int32_t nj = g.nsel > first ? (g.nsel - first + nt - 1) / nt : 0;  // wave-uniform
+      uint32_t raw[kKeyRegs];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int32_t b = b0 + j * nt + (int32_t)threadIdx.x;
-        const int32_t bc = b < g.nvb ? b : g.nvb - 1;
+      for (int j = 0; j < kKeyRegs; ++j) {
+        const int32_t i = first + j * nt + lane;
+        raw[j] = (j < nj && i < g.nvb) ? reinterpret_cast<const uint32_t*>(g.row)[i] : 0u;
+      }
+      select_row_prepare(ctl, area, threadIdx.x, blockDim.x);
+      __syncthreads();  // the loads stay in flight across it
+      LaneKeys lk;
+      lk.nj = nj;
+      lk.cached = true;
+#pragma unroll
+      for (int j = 0; j < kKeyRegs; ++j) {  // the rank keys select_rank_key would give
+        const int32_t i = first + j * nt + lane;
+        uint32_t k;
         if constexpr (KEYS) {  // codes of any NaN stand for the canonical NaN's
-          const uint32_t k = reinterpret_cast<const uint32_t*>(g.row)[bc];
-          v[j] = (k > kKeyPosInf || k < kKeyNegInf) ? kKeyNaN : k;
+          k = (raw[j] > kKeyPosInf || raw[j] < kKeyNegInf) ? kKeyNaN : raw[j];
         } else {
-          v[j] = order_key(g.row[bc]);
+          k = order_key(__uint_as_float(raw[j]));
+        }
+        k = i < g.nvb ? rank_key(k) : 0u;
+        k = i == g.pin ? kKeyPosInf : k;
+        lk.v[j] = (j < nj && i < g.nsel) ? k : 0u;
+      }
+      select_row<true, true, FB, true>(p, r, g, smem, ctl, area, wave, nw, lk);
+    } else {
+      select_row_prepare(ctl, area, threadIdx.x, blockDim.x);
+      for (int32_t b0 = 0; b0 < g.nvb; b0 += 4 * nt) {  // four loads in flight per lane
+        uint32_t v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int32_t b = b0 + j * nt + (int32_t)threadIdx.x;
+          const int32_t bc = b < g.nvb ? b : g.nvb - 1;
+          if constexpr (KEYS) {
+            const uint32_t k = reinterpret_cast<const uint32_t*>(g.row)[bc];
+            v[j] = (k > kKeyPosInf || k < kKeyNegInf) ? kKeyNaN : k;
+          } else {
+            v[j] = order_key(g.row[bc]);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int32_t b = b0 + j * nt + (int32_t)threadIdx.x;
+          if (b < g.nvb) smem[b] = v[j];
         }
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int32_t b = b0 + j * nt + (int32_t)threadIdx.x;
-        if (b < g.nvb) smem[b] = v[j];
-      }
+      __syncthreads();
+      select_row<true, true, FB>(p, r, g, smem, ctl, area, wave, nw);
     }
-    __syncthreads();
-    select_row<true, true>(p, r, g, smem, ctl, area, wave, nw);
     if (r + gridDim.x < p.items) __syncthreads();  // LDS is reused by the next row
   }
 }
@@ -1950,6 +2022,19 @@ namespace {
 
 // dsa_select_from_scores / dsa_select_from_keys: `scores` holds fp32 scores
 // or, with keys, their uint32 codes.
+template <bool KEYS, int FB>
+void* select_scores_fn(bool pre) {
+  return pre ? reinterpret_cast<void*>(&select_scores_kernel<KEYS, FB, true>)
+             : reinterpret_cast<void*>(&select_scores_kernel<KEYS, FB, false>);
+}
+
+template <bool KEYS>
+void* select_scores_fn(int fb, bool pre) {
+  if (fb == kBoundGroups64) return select_scores_fn<KEYS, kBoundGroups64>(pre);
+  if (fb == kBoundGroups128) return select_scores_fn<KEYS, kBoundGroups128>(pre);
+  return select_scores_fn<KEYS, kBoundRadix>(pre);
+}
+
 dsa_status_t select_from_scores_impl(const void* scores, int64_t rows, int64_t nscore,
                                      int64_t ld_scores, int64_t max_global_blocks,
                                      const int32_t* global_row_ke, int32_t row_repeat,
@@ -1990,8 +2075,12 @@ dsa_status_t select_from_scores_impl(const void* scores, int64_t rows, int64_t n
   int64_t waves = cdiv(nblocks, 64);
   const int64_t cap = rows <= 512 ? kWaves : 2;
   if (waves > cap) waves = cap;
-  void* fn = keys ? reinterpret_cast<void*>(&select_scores_kernel<true>)
-                 : reinterpret_cast<void*>(&select_scores_kernel<false>);
+  // the bound select_row would choose for this k and wave count
+  const int fb = topk_blocks <= 32 ? kBoundGroups64
+                 : ((topk_blocks <= 64 && ((waves & 1) == 0 || waves <= 8)) ? kBoundGroups128
+                                                                           : kBoundRadix);
+  const bool pre = cdiv(nblocks, 64 * waves) <= kKeyRegs;  // nsel <= nblocks on every row
+  void* fn = keys ? select_scores_fn<true>(fb, pre) : select_scores_fn<false>(fb, pre);
   return launch(fn, rows, 64 * (int)waves, 1, (size_t)ww * 4, stream, p);
 }
 

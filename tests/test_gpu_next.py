@@ -27,6 +27,7 @@ import torch
 import oracle
 import sparse_attention_kv_dsa_amd as dsa
 from sparse_attention_kv_dsa_amd import workloads
+from bound_rows import bound_rows
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -104,6 +105,34 @@ def test_select_from_scores_row_counts(rows, k):
     w = workloads.ScoresWorkload(f"rows-{rows}-k{k}", x, ends, G, nscore, k, 1)
     got = _gpu_sfs(w, ld_pad=rows % 3)
     assert np.array_equal(got, _oracle_sfs(w))
+
+
+@pytest.mark.parametrize("rows,n", [(100, 1024), (100, 1500), (600, 1024), (600, 1000),
+                                    (600, 1500)])
+def test_select_from_scores_bound_paths(rows, n):
+    """Rows built around the candidate bound (bound_rows): every path of the
+    bound search and the exact fallback, with the rows' keys held in
+    registers (up to 8 per lane) or in LDS, on scores and on their codes."""
+    x = bound_rows(rows, n, rows + n)
+    G = 16
+    rng = np.random.default_rng(n)
+    ends = np.full(rows, n * G, np.int32)   # most rows pin their last block
+    short = rng.random(rows) < 0.3
+    ends[short] = rng.integers(1, n * G, size=int(short.sum()))
+    for k in (64, 40):
+        w = workloads.ScoresWorkload(f"bound-{rows}x{n}-k{k}", x, ends, G, n, k, 1)
+        exp = _oracle_sfs(w)
+        got = _gpu_sfs(w)
+        assert np.array_equal(got, exp), ("scores", rows, n, k)
+        codes = oracle.score_keys(x)
+        expk = np.empty((rows, k), np.int32)
+        oracle.select_from_keys(codes, ends, k, G, n, expk, 1)
+        assert np.array_equal(expk, exp)
+        kd = torch.from_numpy(codes.view(np.int32)).to(DEV)
+        out = torch.full((rows, k), 777, dtype=torch.int32, device=DEV)
+        dsa.select_from_keys(kd, _i32(ends), k, G, n, out, 1)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), exp), ("codes", rows, n, k)
 
 
 @pytest.mark.parametrize("W", [2, 4, 8])

@@ -14,6 +14,7 @@ import torch
 import oracle
 import sparse_attention_kv_dsa_amd as dsa
 from sparse_attention_kv_dsa_amd import workloads
+from bound_rows import bound_rows
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -549,6 +550,28 @@ def test_select_size_boundaries(plan):
             got, sc = gpu_select(w, plan, 3)
             exp_out, exp_sc = oracle_select(w)
             assert_same(got, sc, exp_out, exp_sc, f"n={n} k={k} plan {plan}")
+
+
+@pytest.mark.parametrize("plan", [1, 2, 3, 4])
+def test_select_bound_paths(plan):
+    """Block maxima built around the candidate bound of 32 < k <= 64
+    (tests/bound_rows.py: maxima packed within 2^16 codes, a band that
+    overflows a 16-bit bound into the exact fallback, ties, N(0, 1)) under
+    every plan and an odd and an even wave count: ids and scores as the
+    oracle's."""
+    B = 4
+    for rows, nb in ((8, 1024), (8, 1000), (6, 1500)):
+        s = bound_rows(rows, nb, 7 + nb)
+        x = (np.repeat(s, B, axis=1)
+             - np.tile(np.arange(B, dtype=np.float32), nb)).astype(np.float32)   # block max = s
+        ke = np.full(rows, nb * B, np.int32)
+        ke[1] = nb * B - 5
+        for k in (64, 48):
+            w = workloads.Workload(f"bound-{rows}x{nb}-k{k}", x, None, ke, B, k, 1)
+            exp_out, exp_sc = oracle_select(w)
+            for cb in (3, 4):
+                got, sc = gpu_select(w, plan, cb)
+                assert_same(got, sc, exp_out, exp_sc, f"nb={nb} k={k} plan {plan} arg {cb}")
 
 
 @pytest.mark.parametrize("plan", [1, 2, 3, 4])
