@@ -1227,20 +1227,23 @@ block_scores_kernel(Params p) {
 // wave count), so each instance holds one bound's code.  PRE: every row has
 // at most kKeyRegs keys per lane; the lanes load their keys straight into
 // registers (all loads in flight at once) and the select works from there,
-// with no LDS copy of the row unless it takes the exact fallback.
+// with no LDS copy of the row unless it takes the exact fallback.  NW: the
+// wave count when fixed at compile time (2, the many-rows case; 0: from the
+// launch): 61 instead of 72 VGPRs, eight waves per SIMD, and about a sixth
+// fewer VALU instructions on 8192 rows of 1024 scores (24.8 -> 21.8 us).
 // Seven waves per SIMD (at most 72 VGPRs, no spills): rows' selects share
 // each CU.  On 8192 rows of 1024 scores at k = 64 this took 36.3 -> 31.1 us
 // against the compiler's own choice (83 VGPRs, five waves); six waves gave
 // 32.4, eight spill to scratch and gave 32.0 (measured before FB and PRE;
 // with them six and eight waves are still slower).
-template <bool KEYS, int FB, bool PRE>
-__global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(7)))
+template <bool KEYS, int FB, bool PRE, int NW>
+__global__ void __launch_bounds__(NW ? NW * 64 : 1024) __attribute__((amdgpu_waves_per_eu(7)))
 select_scores_kernel(Params p) {
   extern __shared__ uint32_t smem[];
   const int wave = wave_index();
   const int lane = threadIdx.x & 63;
-  const int nw = blockDim.x >> 6;
-  const int32_t nt = (int32_t)blockDim.x;
+  const int nw = NW ? NW : (int)(blockDim.x >> 6);
+  const int32_t nt = nw * 64;
   uint32_t* ctl = smem + p.keys_words;
   uint32_t* area = ctl + kCtlWords;
   const int32_t ncopy = p.width < p.nblocks ? (int32_t)p.width : p.nblocks;
@@ -2023,16 +2026,17 @@ namespace {
 // dsa_select_from_scores / dsa_select_from_keys: `scores` holds fp32 scores
 // or, with keys, their uint32 codes.
 template <bool KEYS, int FB>
-void* select_scores_fn(bool pre) {
-  return pre ? reinterpret_cast<void*>(&select_scores_kernel<KEYS, FB, true>)
-             : reinterpret_cast<void*>(&select_scores_kernel<KEYS, FB, false>);
+void* select_scores_fn(bool pre, bool two) {
+  if (pre && two) return reinterpret_cast<void*>(&select_scores_kernel<KEYS, FB, true, 2>);
+  return pre ? reinterpret_cast<void*>(&select_scores_kernel<KEYS, FB, true, 0>)
+             : reinterpret_cast<void*>(&select_scores_kernel<KEYS, FB, false, 0>);
 }
 
 template <bool KEYS>
-void* select_scores_fn(int fb, bool pre) {
-  if (fb == kBoundGroups64) return select_scores_fn<KEYS, kBoundGroups64>(pre);
-  if (fb == kBoundGroups128) return select_scores_fn<KEYS, kBoundGroups128>(pre);
-  return select_scores_fn<KEYS, kBoundRadix>(pre);
+void* select_scores_fn(int fb, bool pre, bool two) {
+  if (fb == kBoundGroups64) return select_scores_fn<KEYS, kBoundGroups64>(pre, two);
+  if (fb == kBoundGroups128) return select_scores_fn<KEYS, kBoundGroups128>(pre, two);
+  return select_scores_fn<KEYS, kBoundRadix>(pre, two);
 }
 
 dsa_status_t select_from_scores_impl(const void* scores, int64_t rows, int64_t nscore,
@@ -2080,7 +2084,8 @@ dsa_status_t select_from_scores_impl(const void* scores, int64_t rows, int64_t n
                  : ((topk_blocks <= 64 && ((waves & 1) == 0 || waves <= 8)) ? kBoundGroups128
                                                                            : kBoundRadix);
   const bool pre = cdiv(nblocks, 64 * waves) <= kKeyRegs;  // nsel <= nblocks on every row
-  void* fn = keys ? select_scores_fn<true>(fb, pre) : select_scores_fn<false>(fb, pre);
+  void* fn = keys ? select_scores_fn<true>(fb, pre, waves == 2)
+                 : select_scores_fn<false>(fb, pre, waves == 2);
   return launch(fn, rows, 64 * (int)waves, 1, (size_t)ww * 4, stream, p);
 }
 
