@@ -750,6 +750,14 @@ constexpr int kBoundGroups64 = 0;   // k <= 32
 constexpr int kBoundRadix = 1;      // k > 64
 constexpr int kBoundGroups128 = 2;  // 32 < k <= 64
 
+// The bound select_row uses for k on nw waves (also chosen on the host for
+// kernels compiled for one bound).
+__host__ __device__ inline int select_bound(int32_t k, int nw) {
+  if (k <= 32) return kBoundGroups64;
+  if (k <= 64 && ((nw & 1) == 0 || nw <= 8)) return kBoundGroups128;
+  return kBoundRadix;
+}
+
 // The general path of select_row (nsel > 64).  The candidate bound T0 comes
 // from NG group maxima (NG = 64 or 128), group l holding the keys i with
 // i mod NG == l: T0 = the keff-th largest group maximum (keff <= NG), or
@@ -984,9 +992,10 @@ __device__ __forceinline__ void select_row(const Params& p, int64_t r, const Row
   if constexpr (FB >= 0) {
     select_row_general<WG, FB, KC, PRE>(p, g, keys, ctl, area, out_row, wave, nw, pre);
   } else {
-    if (k <= 32)
+    const int bound = select_bound(k, nw);
+    if (bound == kBoundGroups64)
       select_row_general<WG, kBoundGroups64, KC, PRE>(p, g, keys, ctl, area, out_row, wave, nw, pre);
-    else if (k <= 64 && ((nw & 1) == 0 || nw <= 8))
+    else if (bound == kBoundGroups128)
       select_row_general<WG, kBoundGroups128, KC, PRE>(p, g, keys, ctl, area, out_row, wave, nw, pre);
     else
       select_row_general<WG, kBoundRadix, KC, PRE>(p, g, keys, ctl, area, out_row, wave, nw, pre);
@@ -1014,12 +1023,15 @@ __global__ void __launch_bounds__(kThreads) select_wave_rows_kernel(Params p) {
 }
 
 // Plan "group": all waves of a workgroup stream one row into LDS, then select
-// it together.
-template <int G>
-__global__ void __launch_bounds__(1024) select_group_rows_kernel(Params p) {
+// it together.  NW (wave count) and FB (bound) fixed at compile time, or 0 and
+// -1 for the launch's and k's: the fixed instances for the usual shapes hold
+// fewer registers (4 waves, block size 64: 112 -> 81 VGPRs, five more waves
+// per CU).
+template <int G, int NW = 0, int FB = -1>
+__global__ void __launch_bounds__(NW ? NW * 64 : 1024) select_group_rows_kernel(Params p) {
   extern __shared__ uint32_t smem[];
   const int wave = wave_index();
-  const int nw = blockDim.x >> 6;
+  const int nw = NW ? NW : (int)(blockDim.x >> 6);
   uint32_t* ctl = smem + p.keys_words;
   uint32_t* area = ctl + kCtlWords;
   for (int64_t r = blockIdx.x; r < p.items; r += gridDim.x) {
@@ -1027,7 +1039,7 @@ __global__ void __launch_bounds__(1024) select_group_rows_kernel(Params p) {
     select_row_prepare(ctl, area, threadIdx.x, blockDim.x);
     stream_blocks<G, kUnroll, true, true>(p, g, 0, g.nvb, wave, nw, EmitKey{smem});
     __syncthreads();
-    select_row<true>(p, r, g, smem, ctl, area, wave, nw);
+    select_row<true, false, FB>(p, r, g, smem, ctl, area, wave, nw);
     if (r + gridDim.x < p.items) __syncthreads();  // LDS is reused by the next row
   }
 }
@@ -1104,13 +1116,15 @@ __device__ __forceinline__ uint32_t xcc_id() {
 
 // FULL (chosen on the host): parts of 8 tiles or more per wave skip the
 // masks on interior tiles; short parts measured faster without that test.
-template <int G, bool FULL>
-__global__ void __launch_bounds__(1024) select_pair_rows_kernel(Params p) {
+// NW and FB as in select_group_rows_kernel (8 waves, block size 64: 71 -> 61
+// VGPRs; decode batch 7.98 -> 7.61 us, long-context decode 14.96 -> 14.58).
+template <int G, bool FULL, int NW = 0, int FB = -1>
+__global__ void __launch_bounds__(NW ? NW * 64 : 1024) select_pair_rows_kernel(Params p) {
   extern __shared__ uint32_t smem[];
   const int wave = wave_index();
-  const int nw = blockDim.x >> 6;
+  const int nw = NW ? NW : (int)(blockDim.x >> 6);
   const int tid = threadIdx.x;
-  const int nt = blockDim.x;
+  const int nt = nw * 64;
   const int H = p.parts;
   const int64_t j = p.spread ? blockIdx.x : blockIdx.x >> 3;
   const int64_t r = p.spread ? j / H : (j / H) * 8 + (blockIdx.x & 7);
@@ -1173,7 +1187,7 @@ __global__ void __launch_bounds__(1024) select_pair_rows_kernel(Params p) {
     }
   }
   __syncthreads();
-  select_row<true>(p, r, g, smem, ctl, area, wave, nw);
+  select_row<true, false, FB>(p, r, g, smem, ctl, area, wave, nw);
 }
 
 // Block scores to HBM; item = r * nchunks + c covers blocks
@@ -1585,6 +1599,38 @@ DSA_KERNEL_TABLE(stream_keys_kernel)
   }
 DSA_PAIR_TABLE(select_pair_rows_ptr, false)
 DSA_PAIR_TABLE(select_pair_rows_full_ptr, true)
+
+// Instances with the wave count and bound fixed, for block sizes 64 and 128
+// (G = 16, 32) at the default wave counts; nullptr where none exists.
+template <int G, int NW>
+void* group_fixed(int fb) {
+  if (fb == kBoundGroups64) return reinterpret_cast<void*>(&select_group_rows_kernel<G, NW, kBoundGroups64>);
+  if (fb == kBoundGroups128) return reinterpret_cast<void*>(&select_group_rows_kernel<G, NW, kBoundGroups128>);
+  return reinterpret_cast<void*>(&select_group_rows_kernel<G, NW, kBoundRadix>);
+}
+void* select_group_fixed_ptr(int g, int waves, int32_t k) {
+  if (waves != kWaves) return nullptr;
+  const int fb = select_bound(k, waves);
+  if (g == 16) return group_fixed<16, kWaves>(fb);
+  if (g == 32) return group_fixed<32, kWaves>(fb);
+  return nullptr;
+}
+constexpr int kPairWaves = 8;
+template <int G, bool FULL>
+void* pair_fixed(int fb) {
+  if (fb == kBoundGroups64)
+    return reinterpret_cast<void*>(&select_pair_rows_kernel<G, FULL, kPairWaves, kBoundGroups64>);
+  if (fb == kBoundGroups128)
+    return reinterpret_cast<void*>(&select_pair_rows_kernel<G, FULL, kPairWaves, kBoundGroups128>);
+  return reinterpret_cast<void*>(&select_pair_rows_kernel<G, FULL, kPairWaves, kBoundRadix>);
+}
+void* select_pair_fixed_ptr(int g, bool full, int waves, int32_t k) {
+  if (waves != kPairWaves) return nullptr;
+  const int fb = select_bound(k, waves);
+  if (g == 16) return full ? pair_fixed<16, true>(fb) : pair_fixed<16, false>(fb);
+  if (g == 32) return full ? pair_fixed<32, true>(fb) : pair_fixed<32, false>(fb);
+  return nullptr;
+}
 #define DSA_SCORES_TABLE(NAME, KEYS)                                                  \
   void* NAME(int g) {                                                                 \
     switch (g) {                                                                      \
@@ -1679,7 +1725,7 @@ void pair_shape(int64_t rows, int64_t width, int* parts, int* waves) {
   int64_t n = r8 <= 32 ? 8 : (r8 <= 64 ? 4 : 2);
   const int64_t by_width = width / 8192 > 2 ? width / 8192 : 2;
   *parts = (int)(n < by_width ? n : by_width);
-  *waves = width >= 262144 ? 16 : 8;
+  *waves = width >= 262144 ? 16 : kPairWaves;
 }
 
 // ---------------------------------------------------- static scratch --
@@ -1950,7 +1996,9 @@ dsa_status_t dsa_select_candidate_blocks_plan(
                   64 * (int)nw, (int)nw, wave_lds, stream, p);
   if (plan == kPlanGroup) {
     const int waves = plan_arg > 0 ? plan_arg : kWaves;
-    return launch(select_group_rows_kernel_ptr(g), rows, 64 * waves, 1, (size_t)ww * 4, stream, p);
+    void* fn = select_group_fixed_ptr(g, waves, topk_blocks);
+    if (!fn) fn = select_group_rows_kernel_ptr(g);
+    return launch(fn, rows, 64 * waves, 1, (size_t)ww * 4, stream, p);
   }
   if (plan == kPlanPair) {
     int parts, waves;
@@ -1961,8 +2009,9 @@ dsa_status_t dsa_select_candidate_blocks_plan(
     p.spread = plan_arg >> 16;
     // parts of 8 wave tiles or more per wave take the unmasked interior path
     const int64_t part_units = ((cdiv(nblocks, parts) + 31) / 32) * 32 * g;
-    void* fn = part_units >= 64 * 8 * (int64_t)waves ? select_pair_rows_full_ptr(g)
-                                                      : select_pair_rows_ptr(g);
+    const bool full = part_units >= 64 * 8 * (int64_t)waves;
+    void* fn = select_pair_fixed_ptr(g, full, waves, topk_blocks);
+    if (!fn) fn = full ? select_pair_rows_full_ptr(g) : select_pair_rows_ptr(g);
     return launch(fn, 8 * parts * cdiv(rows, 8), 64 * waves, 1,
                   (size_t)ww * 4, stream, p);
   }
