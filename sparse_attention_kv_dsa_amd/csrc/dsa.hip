@@ -758,6 +758,39 @@ __host__ __device__ inline int select_bound(int32_t k, int nw) {
   return kBoundRadix;
 }
 
+// T0 from group maxima held one (N = 1: 64 groups) or two (N = 2: 128
+// groups) per lane of one wave: the largest value with at least kq maxima at
+// or above it (the kq-th largest maximum), bit by bit from the top, each
+// step a ballot per maximum register.  Any t with at least kq maxima >= t
+// bounds the keff-th key from below; the exact kq-th maximum only trims
+// candidates.  So the search stops after the top 16 bits unless more than
+// kq + kq/4 maxima lie at or above t (maxima packed within 2^16 codes of
+// each other, where the lower bits still separate them).  Each step is a
+// dependent chain of ballots and scalar arithmetic.
+template <int N>
+__device__ __forceinline__ uint32_t maxima_bound(uint32_t g0, uint32_t g1, uint32_t kq) {
+  uint32_t t = 0u, ct = 64u * N;  // ct: maxima >= t (all of them for t = 0)
+#pragma unroll
+  for (int bit = 31; bit >= 16; --bit) {
+    const uint32_t c = t | (1u << bit);
+    uint32_t cnt = (uint32_t)__popcll(__ballot(g0 >= c));
+    if constexpr (N == 2) cnt += (uint32_t)__popcll(__ballot(g1 >= c));
+    if (cnt >= kq) {
+      t = c;
+      ct = cnt;
+    }
+  }
+  if (ct > kq + (kq >> 2)) {  // wave-uniform
+    for (int bit = 15; bit >= 0; --bit) {
+      const uint32_t c = t | (1u << bit);
+      uint32_t cnt = (uint32_t)__popcll(__ballot(g0 >= c));
+      if constexpr (N == 2) cnt += (uint32_t)__popcll(__ballot(g1 >= c));
+      if (cnt >= kq) t = c;
+    }
+  }
+  return t;
+}
+
 // The general path of select_row (nsel > 64).  The candidate bound T0 comes
 // from NG group maxima (NG = 64 or 128), group l holding the keys i with
 // i mod NG == l: T0 = the keff-th largest group maximum (keff <= NG), or
@@ -821,31 +854,7 @@ __device__ __forceinline__ void select_row_general(const Params& p, const RowGeo
         }
       }
       const uint32_t kq = (uint32_t)k < nvalid ? (uint32_t)k : nvalid;
-      // Any t with at least kq maxima >= t bounds the keff-th key from
-      // below; the exact kq-th maximum only trims candidates.  So the search
-      // stops after the top 16 bits unless more than kq + kq/4 maxima lie at
-      // or above t (maxima packed within 2^16 codes of each other, where the
-      // lower bits still separate them).  Each step is a dependent chain of
-      // two ballots and scalar arithmetic in one wave.
-      uint32_t t = 0u, ct = 128u;  // ct: maxima >= t (all 128 for t = 0)
-#pragma unroll
-      for (int bit = 31; bit >= 16; --bit) {
-        const uint32_t c = t | (1u << bit);
-        const uint32_t cnt =
-            (uint32_t)__popcll(__ballot(g0 >= c)) + (uint32_t)__popcll(__ballot(g1 >= c));
-        if (cnt >= kq) {
-          t = c;
-          ct = cnt;
-        }
-      }
-      if (ct > kq + (kq >> 2)) {  // wave-uniform
-        for (int bit = 15; bit >= 0; --bit) {
-          const uint32_t c = t | (1u << bit);
-          const uint32_t cnt =
-              (uint32_t)__popcll(__ballot(g0 >= c)) + (uint32_t)__popcll(__ballot(g1 >= c));
-          if (cnt >= kq) t = c;
-        }
-      }
+      const uint32_t t = maxima_bound<2>(g0, g1, kq);
       if (lane == 0) ctl[kCtlT0] = t;
     }
     row_barrier<WG>();  // T0 is out, and the maxima rows are read before candidates overwrite them
@@ -858,31 +867,38 @@ __device__ __forceinline__ void select_row_general(const Params& p, const RowGeo
       tmax = umax(tmax, rk);
       nv += (uint32_t)__popcll(__ballot(rk != 0u));
     });
-    area[wave * 64 + lane] = tmax;
-    if (lane == 0) ctl[kCtlSlotCount + wave] = nv;
-    row_barrier<WG>();
-    // (C) every wave: the 64 group maxima (maximum over the waves' rows) and
-    // keff; then a slice of the maxima tested against all of them: v
-    // qualifies when #(maxima >= v) >= keff.  The wave's largest qualifying
-    // v goes to its slot.
-    uint32_t gmx = 0u;
-    for (int w = 0; w < nw; ++w) gmx = umax(gmx, area[w * 64 + lane]);
-    nvalid = (uint32_t)__builtin_amdgcn_readlane(
-        (int)row_sum16(lane < nw ? ctl[kCtlSlotCount + lane] : 0u), 0);
-    const uint32_t kq = (uint32_t)k < nvalid ? (uint32_t)k : nvalid;
-    const int32_t len = (64 + nw - 1) / nw;
-    const int32_t l0 = wave * len;
-    const int32_t l1 = l0 + len < 64 ? l0 + len : 64;
-    uint32_t best = 0u;
-    for (int32_t l = l0; l < l1; ++l) {  // wave-uniform
-      const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)gmx, l);
-      const uint32_t c = (uint32_t)__popcll(__ballot(gmx >= v));
-      best = (c >= kq && v > best) ? v : best;
+    if constexpr (!WG) {
+      // one wave holds all 64 maxima: a bit search of at least 16 ballots
+      // instead of testing each maximum against all of them (64 ballots)
+      nvalid = nv;
+      t0 = maxima_bound<1>(tmax, 0u, (uint32_t)k < nvalid ? (uint32_t)k : nvalid);
+    } else {
+      area[wave * 64 + lane] = tmax;
+      if (lane == 0) ctl[kCtlSlotCount + wave] = nv;
+      row_barrier<WG>();
+      // (C) every wave: the 64 group maxima (maximum over the waves' rows) and
+      // keff; then a slice of the maxima tested against all of them: v
+      // qualifies when #(maxima >= v) >= keff.  The wave's largest qualifying
+      // v goes to its slot.
+      uint32_t gmx = 0u;
+      for (int w = 0; w < nw; ++w) gmx = umax(gmx, area[w * 64 + lane]);
+      nvalid = (uint32_t)__builtin_amdgcn_readlane(
+          (int)row_sum16(lane < nw ? ctl[kCtlSlotCount + lane] : 0u), 0);
+      const uint32_t kq = (uint32_t)k < nvalid ? (uint32_t)k : nvalid;
+      const int32_t len = (64 + nw - 1) / nw;
+      const int32_t l0 = wave * len;
+      const int32_t l1 = l0 + len < 64 ? l0 + len : 64;
+      uint32_t best = 0u;
+      for (int32_t l = l0; l < l1; ++l) {  // wave-uniform
+        const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)gmx, l);
+        const uint32_t c = (uint32_t)__popcll(__ballot(gmx >= v));
+        best = (c >= kq && v > best) ? v : best;
+      }
+      if (lane == 0) ctl[kCtlSlotBound + wave] = best;
+      row_barrier<WG>();
+      t0 = (uint32_t)__builtin_amdgcn_readlane(
+          (int)group_umax<16>(lane < nw ? ctl[kCtlSlotBound + lane] : 0u), 0);
     }
-    if (lane == 0) ctl[kCtlSlotBound + wave] = best;
-    row_barrier<WG>();
-    t0 = (uint32_t)__builtin_amdgcn_readlane(
-        (int)group_umax<16>(lane < nw ? ctl[kCtlSlotBound + lane] : 0u), 0);
   }
   const int32_t keff = (uint32_t)k < nvalid ? k : (int32_t)nvalid;
 
