@@ -239,6 +239,31 @@ def test_block_scores_many_rows(seed, rows, width, B, R):
         assert_same(np.zeros(1), got, np.zeros(1), exp, f"{w.name} pin={pin}")
 
 
+@pytest.mark.parametrize("B", [4, 8, 16])
+def test_block_scores_small_blocks_in_chunks(B):
+    """Small blocks, where a chunk's scores are staged in LDS and stored
+    after its streaming: few long rows (many chunks per row, chunk offsets
+    past 0), and many rows of one whole-row chunk; windows empty, ragged,
+    clipped or whole; scores and codes as the oracle's."""
+    for rows, width, seed in ((5, 300001, 31), (1100, 8200, 32)):
+        w = workloads.many_rows_case(seed + B, rows, width, B, 1)
+        _say("block scores", w.name)
+        x = dev_logits(w.logits, 1, offset=4)
+        for pin in (True, False):
+            got = dsa.block_scores(x, dev_i32(w.row_ks), dev_i32(w.row_ke), B, 1,
+                                   pin_newest=pin).cpu().numpy()
+            exp = oracle.block_scores(w.logits, w.row_ks, w.row_ke, B, 1, pin_newest=pin,
+                                      nthreads=HOST_THREADS)
+            assert_same(np.zeros(1), got, np.zeros(1), exp, f"{w.name} pin={pin}")
+            codes = dsa.block_score_keys(x, dev_i32(w.row_ks), dev_i32(w.row_ke), B, 1,
+                                         pin_newest=pin)
+            torch.cuda.synchronize()
+            expk = oracle.block_score_keys(w.logits, w.row_ks, w.row_ke, B, 1, pin_newest=pin,
+                                           nthreads=HOST_THREADS)
+            assert np.array_equal(codes.view(torch.int32).cpu().numpy().view(np.uint32), expk), (
+                w.name, pin)
+
+
 def test_random_many_rows():
     """Random shapes around the block scores' plan thresholds (1024 rows,
     32K columns): scores and ids of every row bit-exact, B from 1 to 300,
