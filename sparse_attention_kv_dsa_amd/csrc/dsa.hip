@@ -1081,8 +1081,8 @@ __global__ void __launch_bounds__(kThreads) select_wave_rows_kernel(Params p) {
 // Plan "group": all waves of a workgroup stream one row into LDS, then select
 // it together.  NW (wave count) and FB (bound) fixed at compile time, or 0 and
 // -1 for the launch's and k's: the fixed instances for the usual shapes hold
-// fewer registers (4 waves, block size 64: 112 -> 81 VGPRs, five more waves
-// per CU).
+// fewer registers (4 waves, block size 64: 112 -> 81 VGPRs, five waves per
+// SIMD instead of four).
 template <int G, int NW = 0, int FB = -1>
 __global__ void __launch_bounds__(NW ? NW * 64 : 1024) select_group_rows_kernel(Params p) {
   extern __shared__ uint32_t smem[];
@@ -1173,7 +1173,7 @@ __device__ __forceinline__ uint32_t xcc_id() {
 // FULL (chosen on the host): parts of 8 tiles or more per wave skip the
 // masks on interior tiles; short parts measured faster without that test.
 // NW and FB as in select_group_rows_kernel (8 waves, block size 64: 71 -> 61
-// VGPRs; decode batch 7.98 -> 7.61 us, long-context decode 14.96 -> 14.58).
+// VGPRs; decode batch 7.92 -> 7.73 us, long-context decode 14.98 -> 14.76).
 template <int G, bool FULL, int NW = 0, int FB = -1>
 __global__ void __launch_bounds__(NW ? NW * 64 : 1024) select_pair_rows_kernel(Params p) {
   extern __shared__ uint32_t smem[];
