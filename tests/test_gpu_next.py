@@ -308,7 +308,7 @@ def test_mask_random_cases(seed):
         R = int(rng.integers(1, 3))
         width = int(rng.integers(1, 20000))
         B = int(rng.choice([1, 3, 4, 7, 16, 64, 100, 128]))
-        k = int(rng.integers(0, 40))
+        k = int(rng.integers(0, 40)) if rng.random() < 0.7 else int(rng.integers(60, 130))
         groups = -(-rows // R)
         x = rng.standard_normal((rows, width)).astype(np.float32)
         x[rng.random((rows, width)) < 1e-3] = np.nan
