@@ -111,15 +111,16 @@ def test_select_from_scores_row_counts(rows, k):
                                     (600, 1500)])
 def test_select_from_scores_bound_paths(rows, n):
     """Rows built around the candidate bound (bound_rows): every path of the
-    bound search and the exact fallback, with the rows' keys held in
-    registers (up to 8 per lane) or in LDS, on scores and on their codes."""
+    bound search (128 groups for 32 < k <= 64, 64 groups below) and the
+    exact fallback, with the rows' keys held in registers (up to 8 per lane)
+    or in LDS, on scores and on their codes."""
     x = bound_rows(rows, n, rows + n)
     G = 16
     rng = np.random.default_rng(n)
     ends = np.full(rows, n * G, np.int32)   # most rows pin their last block
     short = rng.random(rows) < 0.3
     ends[short] = rng.integers(1, n * G, size=int(short.sum()))
-    for k in (64, 40):
+    for k in (64, 40, 32, 16):   # 128 groups, then 64
         w = workloads.ScoresWorkload(f"bound-{rows}x{n}-k{k}", x, ends, G, n, k, 1)
         exp = _oracle_sfs(w)
         got = _gpu_sfs(w)

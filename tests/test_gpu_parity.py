@@ -579,11 +579,11 @@ def test_select_size_boundaries(plan):
 
 @pytest.mark.parametrize("plan", [1, 2, 3, 4])
 def test_select_bound_paths(plan):
-    """Block maxima built around the candidate bound of 32 < k <= 64
-    (tests/bound_rows.py: maxima packed within 2^16 codes, a band that
-    overflows a 16-bit bound into the exact fallback, ties, N(0, 1)) under
-    every plan and an odd and an even wave count: ids and scores as the
-    oracle's."""
+    """Block maxima built around the candidate bound (tests/bound_rows.py:
+    maxima packed within 2^16 codes, a band that overflows a 16-bit bound
+    into the exact fallback, ties, N(0, 1)) for k with 128 groups (48, 64)
+    and with 64 (16, 32), under every plan and an odd and an even wave
+    count: ids and scores as the oracle's."""
     B = 4
     for rows, nb in ((8, 1024), (8, 1000), (6, 1500)):
         s = bound_rows(rows, nb, 7 + nb)
@@ -591,7 +591,7 @@ def test_select_bound_paths(plan):
              - np.tile(np.arange(B, dtype=np.float32), nb)).astype(np.float32)   # block max = s
         ke = np.full(rows, nb * B, np.int32)
         ke[1] = nb * B - 5
-        for k in (64, 48):
+        for k in (64, 48, 32, 16):   # 128 groups, then 64
             w = workloads.Workload(f"bound-{rows}x{nb}-k{k}", x, None, ke, B, k, 1)
             exp_out, exp_sc = oracle_select(w)
             for cb in (3, 4):
