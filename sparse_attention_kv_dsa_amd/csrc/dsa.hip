@@ -1350,7 +1350,9 @@ select_scores_kernel(Params p) {
 #pragma unroll
       for (int j = 0; j < kKeyRegs; ++j) {
         const int32_t i = first + j * nt + lane;
-        raw[j] = (j < nj && i < g.nvb) ? reinterpret_cast<const uint32_t*>(g.row)[i] : 0u;
+        // past the row's columns: -inf, whose rank key is 0 ("no candidate")
+        raw[j] = (j < nj && i < g.nvb) ? reinterpret_cast<const uint32_t*>(g.row)[i]
+                                       : (KEYS ? kKeyNegInf : 0xFF800000u);
       }
       select_row_prepare(ctl, area, threadIdx.x, blockDim.x);
       __syncthreads();  // the loads stay in flight across it
@@ -1366,9 +1368,7 @@ select_scores_kernel(Params p) {
         } else {
           k = order_key(__uint_as_float(raw[j]));
         }
-        k = i < g.nvb ? rank_key(k) : 0u;
-        k = i == g.pin ? kKeyPosInf : k;
-        lk.v[j] = (j < nj && i < g.nsel) ? k : 0u;
+        lk.v[j] = i == g.pin ? kKeyPosInf : rank_key(k);  // the pin lies below nsel
       }
       select_row<true, true, FB, true>(p, r, g, smem, ctl, area, wave, nw, lk);
     } else {
