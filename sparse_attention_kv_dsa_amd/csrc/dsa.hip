@@ -847,12 +847,12 @@ __device__ __forceinline__ void select_row_general(const Params& p, const RowGeo
     // even wave count always the wave's parity (one maxima row per wave),
     // with an odd one (nw <= 8) alternately (two rows per wave).
     uint32_t m0 = 0u, m1 = 0u, nv = 0u;
+    const bool two_rows = (nw & 1) != 0;
     for_lane_keys(lk, keys, g, wave, nt, [&](int32_t i, uint32_t rk) {
-      if ((i >> 6) & 1) m1 = umax(m1, rk);
-      else m0 = umax(m0, rk);
+      if (two_rows && ((i >> 6) & 1)) m1 = umax(m1, rk);
+      else m0 = umax(m0, rk);  // one half per wave for an even wave count
       nv += (uint32_t)__popcll(__ballot(rk != 0u));
     });
-    const bool two_rows = (nw & 1) != 0;
     if (two_rows) {
       area[(2 * wave) * 64 + lane] = m0;
       area[(2 * wave + 1) * 64 + lane] = m1;
