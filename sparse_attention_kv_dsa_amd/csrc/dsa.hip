@@ -1974,18 +1974,21 @@ dsa_status_t block_scores_impl(const float* logits, int64_t rows, int64_t width,
   p.nblocks = (int32_t)nblocks;
   // Items are row chunks: 8K columns, doubled until at most 512 items
   // remain (few rows: chunks spread each row over many CUs), or whole rows
-  // from 1024 rows on.  Whole rows take one wave below 32K columns (short
+  // from 1024 rows on.  Whole rows take two waves below 32K columns (short
   // windows: more rows in flight per CU), else four.  Measured against fixed
   // 8K chunks of four waves: large prefill 8192x65536 300 -> 172 us, prefill
   // chunk 4096x16384 32 -> 13.5, 8192x8192 at B = 8 35 -> 30.5, 128x131072
-  // 13.4 -> 11.7; 64x32768 unchanged at 4.5.
+  // 13.4 -> 11.7; 64x32768 unchanged at 4.5.  Two waves instead of one for
+  // the short rows: 8192x4096 at B = 8 26.95 -> 25.5 us, 2048x16384 at
+  // B = 16 25.4 -> 24.5, 8192x8192 at B = 8 50.1 -> 49.5 (full windows),
+  // B = 64 unchanged; four waves were slower.
   const int g = lanes_per_block(block_size);
   int64_t ccols = 8192;
   while (ccols < width && cdiv(width, ccols) > 512 / rows) ccols *= 2;  // rows * chunks > 512
   int64_t cb = rows >= 1024 ? nblocks : cdiv(ccols, block_size);
   if (g > 0) cb = cdiv(cb, 64 / g) * (64 / g);
   if (cb > nblocks) cb = nblocks;
-  const int threads = rows >= 1024 && width < 32768 ? 64 : kThreads;
+  const int threads = rows >= 1024 && width < 32768 ? 128 : kThreads;
   p.chunk_blocks = (int32_t)cb;
   p.nchunks = (int32_t)cdiv(nblocks, cb);
   p.scores = static_cast<float*>(scores);

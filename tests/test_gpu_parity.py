@@ -223,8 +223,8 @@ def test_block_scores_configs():
 @pytest.mark.parametrize("seed,rows,width,B,R", [
     (1, 1100, 33000, 64, 1),   # >= 1024 rows, >= 32K columns: whole rows, four waves
     (2, 2048, 32768, 128, 2),
-    (3, 1030, 5003, 7, 1),     # one-wave whole rows on the any-alignment path
-    (4, 1024, 16384, 8, 3),    # one-wave whole rows, vector path
+    (3, 1030, 5003, 7, 1),     # two-wave whole rows on the any-alignment path
+    (4, 1024, 16384, 8, 3),    # two-wave whole rows, vector path
     (5, 1023, 40000, 16, 1),   # just under 1024 rows: chunks
 ])
 def test_block_scores_many_rows(seed, rows, width, B, R):
