@@ -493,6 +493,40 @@ __device__ __forceinline__ void rank_candidates(const uint64_t* cand, int32_t nc
   }
 }
 
+// ncand <= 64 candidates on nw = 2-8 waves: every wave ranks all of them
+// against its own share of the list (one to four rounds of broadcast reads
+// instead of ncand / 8 dependent rounds in one wave); the partial counts
+// meet in `part` (nw rows of 64 words) and wave 0 adds them up and stores.
+// Holds a workgroup barrier.  Decode batch 7.53 -> 7.22 us, long-context
+// decode 14.59 -> 14.43, against rank_candidates in wave 0 alone.
+__device__ __forceinline__ void rank_candidates_split(const uint64_t* cand, int32_t ncand,
+                                                      int32_t keff, int32_t* out_row,
+                                                      uint32_t* part, int wave, int nw) {
+  const int lane = threadIdx.x & 63;
+  const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(cand);
+  const uint64_t ci = lane < ncand ? cand[lane] : 0ull;
+  const int32_t per = (((ncand + nw - 1) / nw) + 7) & ~7;  // a multiple of 8
+  const int32_t j0 = wave * per;
+  const int32_t j1 = j0 + per < ncand ? j0 + per : ncand;
+  uint32_t r = 0;
+  for (int32_t j = j0; j < j1; j += 8) {  // words past j1 (below 64) are masked
+    const ulonglong2 a = c2[(j >> 1) + 0], b = c2[(j >> 1) + 1];
+    const ulonglong2 c = c2[(j >> 1) + 2], d = c2[(j >> 1) + 3];
+    const int32_t m = j1 - j;  // wave-uniform, >= 1
+    r += (uint32_t)(a.x > ci) + (uint32_t)(m > 1 && a.y > ci) + (uint32_t)(m > 2 && b.x > ci) +
+         (uint32_t)(m > 3 && b.y > ci) + (uint32_t)(m > 4 && c.x > ci) +
+         (uint32_t)(m > 5 && c.y > ci) + (uint32_t)(m > 6 && d.x > ci) +
+         (uint32_t)(m > 7 && d.y > ci);
+  }
+  part[wave * 64 + lane] = r;
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t t = 0;
+    for (int w = 0; w < nw; ++w) t += part[w * 64 + lane];
+    if (lane < ncand && t < (uint32_t)keff) out_row[t] = (int32_t)(~(uint32_t)ci);
+  }
+}
+
 // Radix select (8-bit digits from the top) over the LDS rank keys of one
 // wave's slot array (slot j of lane l is key j*64 + l): the selection is every
 // key >= tg, then the first need_eq keys equal to T in id order.
@@ -988,7 +1022,11 @@ __device__ __forceinline__ void select_row_general(const Params& p, const RowGeo
 
   // (G) rank the candidates, or fall back to the exact one-wave select.
   const int32_t ncand = (int32_t)ctl[kCtlCand];
-  if (ncand <= kCandCap) {
+  if (past && nw >= 2 && ncand <= 64) {  // workgroup-uniform
+    // the maxima rows are dead past the compaction's barrier
+    rank_candidates_split(cand, ncand, keff, out_row, area, wave, nw);
+    for (int32_t j = keff + tid; j < k; j += nt) out_row[j] = -1;
+  } else if (ncand <= kCandCap) {
     rank_candidates(cand, ncand, keff, out_row, wave, nw);
     for (int32_t j = keff + tid; j < k; j += nt) out_row[j] = -1;
   } else {

@@ -33,3 +33,29 @@ def bound_rows(rows, n, seed):
         elif kind == 2:
             x[r] = np.float32(0.75)
     return x
+
+
+def counted_rows(nb, k, extras, seed):
+    """Block scores of rows whose candidate count at the 64-group bound of
+    selects with k <= 32 (block i in group i mod 64) is k + 1 + extras[r]:
+    group l < 63 peaks at 100 + l in block l, group 63 holds 163 and the
+    pinned newest block nb - 1 (nb = 64 m, the row's whole width), so the
+    k-th largest group maximum is 164 - k; the extras are scores in
+    [164 - k, 164 - k + 4) placed, in pairs of equal values, in other blocks
+    of groups that peak above them; every other score is N(0, 1).  The
+    counts straddle the 64 candidates that one wave's lanes hold."""
+    assert nb % 64 == 0 and nb >= 512 and 1 <= k <= 32
+    rng = np.random.default_rng(seed)
+    t0 = 164.0 - k
+    rows = []
+    for x_count in extras:
+        s = rng.standard_normal(nb).astype(np.float32)
+        s[:64] = 100.0 + np.arange(64, dtype=np.float32)
+        vals = t0 + 0.0625 * (np.arange(x_count) // 2)
+        groups = [g for g in range(63) if 100.0 + g > t0 + 4.0]
+        assert len(groups) * (nb // 64 - 1) >= x_count
+        for j, v in enumerate(vals):
+            g = groups[j % len(groups)]
+            s[g + 64 * (1 + j // len(groups))] = v
+        rows.append(s)
+    return np.stack(rows).astype(np.float32)

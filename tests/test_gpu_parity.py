@@ -14,7 +14,7 @@ import torch
 import oracle
 import sparse_attention_kv_dsa_amd as dsa
 from sparse_attention_kv_dsa_amd import workloads
-from bound_rows import bound_rows
+from bound_rows import bound_rows, counted_rows
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -597,6 +597,29 @@ def test_select_bound_paths(plan):
             for cb in (3, 4):
                 got, sc = gpu_select(w, plan, cb)
                 assert_same(got, sc, exp_out, exp_sc, f"nb={nb} k={k} plan {plan} arg {cb}")
+
+
+@pytest.mark.parametrize("plan", [1, 2, 3, 4])
+def test_candidate_counts_around_one_wave(plan):
+    """Rows whose candidate count at the 64-group bound (k <= 32) is set
+    exactly (tests/bound_rows.py: counted_rows): 17 to 133 candidates,
+    straddling the 64 that one wave ranks per pass (up to 64 candidates the
+    workgroup selects of up to 8 waves split the rank over their waves),
+    with tied scores among them; every plan, 2-9 waves for the group plan,
+    assorted waves and parts for the pair plan."""
+    B, nb = 4, 512
+    for k, extras in ((32, (0, 1, 30, 31, 32, 33, 60, 100)),
+                      (16, (0, 1, 40, 46, 47, 48, 49, 64)),
+                      (24, (0, 30, 31, 32, 33, 39, 40))):
+        s = counted_rows(nb, k, extras, 40 + k)
+        x = (np.repeat(s, B, axis=1)
+             - np.tile(np.arange(B, dtype=np.float32), nb)).astype(np.float32)   # block max = s
+        ke = np.full(len(extras), nb * B, np.int32)
+        w = workloads.Workload(f"counted-k{k}", x, None, ke, B, k, 1)
+        exp_out, exp_sc = oracle_select(w)
+        for cb in {1: (2, 3, 4, 8, 9), 4: (0, 1, 2, 4, 6, 8)}.get(plan, (0, 3)):
+            got, sc = gpu_select(w, plan, cb)
+            assert_same(got, sc, exp_out, exp_sc, f"k={k} plan {plan} arg {cb}")
 
 
 @pytest.mark.parametrize("plan", [1, 2, 3, 4])
