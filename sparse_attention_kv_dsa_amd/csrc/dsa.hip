@@ -168,8 +168,15 @@ __device__ __forceinline__ int64_t div_bound(int64_t n, int32_t d) {
   return n / d;
 }
 
-// Called by every lane of a wave (uniform control flow).
+// Called by every lane of a wave (uniform control flow).  G > 0: the
+// block size is 4*G, a power of two, and the divides by it are shifts.
+template <int G = 0>
 __device__ __forceinline__ RowGeom row_geom(const Params& p, int64_t r, bool pin) {
+  // n >= 0
+  auto div_b = [&](int64_t n) -> int64_t {
+    if constexpr (G > 0) return n >> __builtin_ctz(4 * G);
+    else return div_bound(n, p.B);
+  };
   RowGeom g;
   // rows < 2^31: a 32-bit divide, none for row_repeat 1
   const int64_t grp = p.R == 1 ? r : (int64_t)((uint32_t)r / (uint32_t)p.R);
@@ -183,12 +190,12 @@ __device__ __forceinline__ RowGeom row_geom(const Params& p, int64_t r, bool pin
   g.lo = g.s > 0 ? g.s : 0;
   g.hi = e < p.width ? e : p.width;
   int64_t nvb = 0;
-  if (g.hi > g.lo) nvb = div_bound(g.hi - g.s + p.B - 1, p.B);
+  if (g.hi > g.lo) nvb = div_b(g.hi - g.s + p.B - 1);
   if (nvb > p.nblocks) nvb = p.nblocks;
   g.nvb = (int32_t)nvb;
   g.pin = -1;
   if (pin && e > g.s) {
-    const int64_t q = div_bound(e - g.s - 1, p.B);
+    const int64_t q = div_b(e - g.s - 1);
     if (q < p.nblocks) g.pin = (int32_t)q;
   }
   g.nsel = g.nvb > g.pin + 1 ? g.nvb : g.pin + 1;
@@ -1107,7 +1114,7 @@ __global__ void __launch_bounds__(kThreads) select_wave_rows_kernel(Params p) {
   uint32_t* ctl = keys + p.keys_words;
   uint32_t* area = ctl + kCtlWords;
   for (int64_t r = (int64_t)blockIdx.x * nw + wave; r < p.items; r += (int64_t)gridDim.x * nw) {
-    const RowGeom g = row_geom(p, r, true);
+    const RowGeom g = row_geom<G>(p, r, true);
     select_row_prepare(ctl, area, threadIdx.x & 63, 64);
     stream_blocks<G, U, true, true>(p, g, 0, g.nvb, 0, 1, EmitKey{keys});
     wave_sync();
@@ -1129,6 +1136,9 @@ __global__ void __launch_bounds__(NW ? NW * 64 : 1024) select_group_rows_kernel(
   uint32_t* ctl = smem + p.keys_words;
   uint32_t* area = ctl + kCtlWords;
   for (int64_t r = blockIdx.x; r < p.items; r += gridDim.x) {
+    // the divides by the block size kept here: the shifts of row_geom<G>
+    // measured 151.5 -> 152.3 us on the large prefill (they took 1-2.5 %
+    // off the wave and pair plans)
     const RowGeom g = row_geom(p, r, true);
     select_row_prepare(ctl, area, threadIdx.x, blockDim.x);
     stream_blocks<G, kUnroll, true, true>(p, g, 0, g.nvb, wave, nw, EmitKey{smem});
@@ -1148,9 +1158,10 @@ __global__ void __launch_bounds__(kThreads) stream_keys_kernel(Params p) {
   const int wave = wave_index();
   const int nw = blockDim.x >> 6;
   for (int64_t item = blockIdx.x; item < p.items; item += gridDim.x) {
-    const int64_t r = item / p.nchunks;
+    // items < 2^31 (checked on the host): a 32-bit divide
+    const int64_t r = (int64_t)((uint32_t)item / (uint32_t)p.nchunks);
     const int32_t c = (int32_t)(item - r * p.nchunks);
-    const RowGeom g = row_geom(p, r, true);
+    const RowGeom g = row_geom<G>(p, r, true);
     const int32_t b0 = c * p.chunk_blocks;
     if (b0 >= g.nvb) continue;
     const int32_t b1 = b0 + p.chunk_blocks < g.nvb ? b0 + p.chunk_blocks : g.nvb;
@@ -1220,24 +1231,25 @@ __global__ void __launch_bounds__(NW ? NW * 64 : 1024) select_pair_rows_kernel(P
   const int tid = threadIdx.x;
   const int nt = nw * 64;
   const int H = p.parts;
-  const int64_t j = p.spread ? blockIdx.x : blockIdx.x >> 3;
-  const int64_t r = p.spread ? j / H : (j / H) * 8 + (blockIdx.x & 7);
-  const int part = (int)(j % H);
+  const uint32_t j = p.spread ? blockIdx.x : blockIdx.x >> 3;
+  const uint32_t jh = j / (uint32_t)H;
+  const int64_t r = p.spread ? (int64_t)jh : (int64_t)jh * 8 + (blockIdx.x & 7);
+  const int part = (int)(j - jh * (uint32_t)H);
   if (r >= p.rows) return;
   uint32_t* ctl = smem + p.keys_words;
   uint32_t* area = ctl + kCtlWords;
   uint64_t* s_old = reinterpret_cast<uint64_t*>(ctl + kCtlArrival);
-  const RowGeom g = row_geom(p, r, true);
-  // parts of a fixed size (the widest row's share, whole 32-key lines), so
-  // that every busy workgroup streams about the same bytes; a shorter row
-  // uses fewer of its parts and the others leave at once
-  const int32_t cb = (((p.nblocks + H - 1) / H) + 31) & ~31;
-  const int HP = g.nvb > 0 ? (g.nvb + cb - 1) / cb : 1;
-  if (part >= HP) return;
+  const RowGeom g = row_geom<G>(p, r, true);
+  // parts of a fixed size (the widest row's share, whole 32-key lines, set
+  // on the host), so that every busy workgroup streams about the same bytes;
+  // a shorter row uses fewer of its parts and the others leave at once
+  const int32_t cb = p.chunk_blocks;
+  if (part > 0 && (int64_t)part * cb >= g.nvb) return;  // no divide before the loads
   select_row_prepare(ctl, area, tid, nt);
   const int32_t b0 = part * cb < g.nvb ? part * cb : g.nvb;
   const int32_t b1 = b0 + cb < g.nvb ? b0 + cb : g.nvb;
   stream_blocks<G, kUnroll, true, FULL>(p, g, b0, b1, wave, nw, EmitKey{smem});
+  const int HP = g.nvb > 0 ? (g.nvb + cb - 1) / cb : 1;  // parts the row uses
   if (HP > 1) {  // workgroup-uniform; a row of one part needs no hand-off
     __syncthreads();
     uint32_t* wrow = p.ws_keys + r * p.ws_ld;
@@ -1302,9 +1314,12 @@ block_scores_kernel(Params p) {
   const int wave = wave_index();
   const int nw = blockDim.x >> 6;
   for (int64_t item = blockIdx.x; item < p.items; item += gridDim.x) {
-    const int64_t r = item / p.nchunks;
+    // one chunk per row from 1024 rows on; else a 32-bit divide when it fits
+    const int64_t r = p.nchunks == 1 ? item
+                      : ((item >> 32) == 0 ? (int64_t)((uint32_t)item / (uint32_t)p.nchunks)
+                                           : item / p.nchunks);
     const int32_t c = (int32_t)(item - r * p.nchunks);
-    const RowGeom g = row_geom(p, r, p.pin != 0);
+    const RowGeom g = row_geom<G>(p, r, p.pin != 0);
     const int32_t b0 = c * p.chunk_blocks;
     const int32_t b1 = b0 + p.chunk_blocks < p.nblocks ? b0 + p.chunk_blocks : p.nblocks;
     const int32_t sb1 = b1 < g.nvb ? b1 : g.nvb;
@@ -2161,6 +2176,7 @@ dsa_status_t dsa_select_candidate_blocks_plan(
     if (plan_arg & 255) waves = plan_arg & 255;
     p.parts = parts;
     p.spread = plan_arg >> 16;
+    p.chunk_blocks = (int32_t)(((cdiv(nblocks, parts)) + 31) / 32 * 32);  // blocks per part
     // parts of 8 wave tiles or more per wave take the unmasked interior path
     const int64_t part_units = ((cdiv(nblocks, parts) + 31) / 32) * 32 * g;
     const bool full = part_units >= 64 * 8 * (int64_t)waves;
