@@ -147,6 +147,8 @@ struct Params {
   uint64_t* ws_count; // pair plan: per-row arrival counters, zero between calls
   int32_t parts;      // pair plan: workgroups per row
   int32_t spread;     // pair plan: a row's parts on consecutive workgroups (other XCDs)
+  int32_t r_shift;    // log2(R) when R is a power of two, else -1
+  int32_t h_shift;    // pair plan: log2(parts) when a power of two, else -1
   int64_t items;      // work items of the launch
 };
 
@@ -168,6 +170,13 @@ __device__ __forceinline__ int64_t div_bound(int64_t n, int32_t d) {
   return n / d;
 }
 
+// Row group (the bounds index) of row r < 2^31: a shift for a power-of-two
+// row_repeat, else a 32-bit divide.
+__device__ __forceinline__ int64_t row_group(const Params& p, int64_t r) {
+  if (p.r_shift >= 0) return r >> p.r_shift;
+  return (int64_t)((uint32_t)r / (uint32_t)p.R);
+}
+
 // Called by every lane of a wave (uniform control flow).  G > 0: the
 // block size is 4*G, a power of two, and the divides by it are shifts.
 template <int G = 0>
@@ -178,8 +187,7 @@ __device__ __forceinline__ RowGeom row_geom(const Params& p, int64_t r, bool pin
     else return div_bound(n, p.B);
   };
   RowGeom g;
-  // rows < 2^31: a 32-bit divide, none for row_repeat 1
-  const int64_t grp = p.R == 1 ? r : (int64_t)((uint32_t)r / (uint32_t)p.R);
+  const int64_t grp = row_group(p, r);
   // one load brings both bounds (lane 0: the start, the others: the end),
   // one memory round trip instead of two; every lane of the wave is active
   const int32_t* bp = ((threadIdx.x & 63) == 0 && p.ks) ? p.ks + grp : p.ke + grp;
@@ -1232,7 +1240,7 @@ __global__ void __launch_bounds__(NW ? NW * 64 : 1024) select_pair_rows_kernel(P
   const int nt = nw * 64;
   const int H = p.parts;
   const uint32_t j = p.spread ? blockIdx.x : blockIdx.x >> 3;
-  const uint32_t jh = j / (uint32_t)H;
+  const uint32_t jh = p.h_shift >= 0 ? j >> p.h_shift : j / (uint32_t)H;
   const int64_t r = p.spread ? (int64_t)jh : (int64_t)jh * 8 + (blockIdx.x & 7);
   const int part = (int)(j - jh * (uint32_t)H);
   if (r >= p.rows) return;
@@ -1381,7 +1389,7 @@ select_scores_kernel(Params p) {
   uint32_t* area = ctl + kCtlWords;
   const int32_t ncopy = p.width < p.nblocks ? (int32_t)p.width : p.nblocks;
   for (int64_t r = blockIdx.x; r < p.items; r += gridDim.x) {
-    const int64_t e = (int64_t)p.ke[r / p.R];
+    const int64_t e = (int64_t)p.ke[row_group(p, r)];
     RowGeom g;
     g.row = p.logits + r * p.ld;
     g.s = 0;
@@ -1688,6 +1696,11 @@ __global__ void __launch_bounds__(kThreads) fill_minus_one_kernel(int32_t* out, 
 }
 
 // ------------------------------------------------------------------ host --
+
+// log2(v) for a power of two v >= 1, else -1.
+int32_t pow2_shift(int64_t v) {
+  return v > 0 && (v & (v - 1)) == 0 ? (int32_t)__builtin_ctzll((unsigned long long)v) : -1;
+}
 
 // Lanes per block for the vector path: B = 4*G with G a power of two <= 64;
 // 0 selects the scalar path for every row.
@@ -2023,6 +2036,7 @@ dsa_status_t block_scores_impl(const float* logits, int64_t rows, int64_t width,
   p.ke = row_ke;
   p.B = block_size;
   p.R = row_repeat;
+  p.r_shift = pow2_shift(row_repeat);
   p.pin = pin_newest;
   p.nblocks = (int32_t)nblocks;
   // Items are row chunks: 8K columns, doubled until at most 512 items
@@ -2136,6 +2150,7 @@ dsa_status_t dsa_select_candidate_blocks_plan(
   p.ke = row_ke;
   p.B = block_size;
   p.R = row_repeat;
+  p.r_shift = pow2_shift(row_repeat);
   p.pin = 1;
   p.k = topk_blocks;
   p.nblocks = (int32_t)nblocks;
@@ -2175,6 +2190,7 @@ dsa_status_t dsa_select_candidate_blocks_plan(
     if ((plan_arg >> 8) & 255) parts = (plan_arg >> 8) & 255;
     if (plan_arg & 255) waves = plan_arg & 255;
     p.parts = parts;
+    p.h_shift = pow2_shift(parts);
     p.spread = plan_arg >> 16;
     p.chunk_blocks = (int32_t)(((cdiv(nblocks, parts)) + 31) / 32 * 32);  // blocks per part
     // parts of 8 wave tiles or more per wave take the unmasked interior path
@@ -2283,6 +2299,7 @@ dsa_status_t select_from_scores_impl(const void* scores, int64_t rows, int64_t n
   p.ke = global_row_ke;
   p.B = global_block_size;
   p.R = row_repeat;
+  p.r_shift = pow2_shift(row_repeat);
   p.pin = 1;
   p.k = topk_blocks;
   p.nblocks = (int32_t)nblocks;
