@@ -688,12 +688,14 @@ __device__ __forceinline__ uint32_t select_rank_key(const uint32_t* keys, const 
   return i < g.nsel ? rank_key(key) : 0u;
 }
 
-// Clears the LDS state select_row expects zeroed: the group maxima (the first
-// 256 words of `area`) and the control counters.  Call before the barrier
-// that precedes select_row (the streaming never touches these words).
+// Clears the LDS state select_row expects zeroed: the first 256 words of
+// `area` (the radix histogram) and the control counters below the per-wave
+// slots.  Thread t clears area[t] (and area[t + nt]): with nt = 128 each wave
+// clears its own maxima row.  Call before the barrier that precedes
+// select_row (the streaming never touches these words).
 __device__ __forceinline__ void select_row_prepare(uint32_t* ctl, uint32_t* area, int tid, int nt) {
   for (int t = tid; t < 256; t += nt) area[t] = 0u;
-  if (tid < kCtlWords) ctl[tid] = 0u;
+  if (tid < kCtlSlotCount) ctl[tid] = 0u;  // per-wave slots are written before they are read
 }
 
 // A lane's rank keys of one row, read from LDS once when the row has at most
@@ -1438,7 +1440,13 @@ select_scores_kernel(Params p) {
                                        : (KEYS ? kKeyNegInf : 0xFF800000u);
       }
       select_row_prepare(ctl, area, threadIdx.x, blockDim.x);
-      __syncthreads();  // the loads stay in flight across it
+      // two waves under a group-maxima bound: each wave zeroes only LDS words
+      // it writes itself or that are written after the select's first
+      // barrier, so no barrier is needed here (DCP select 21.22 -> 21.12 us);
+      // the direct rank (<= 64 keys) and the radix bound read zeroed words
+      // of the other wave first
+      if (!(NW == 2 && (FB == kBoundGroups64 || FB == kBoundGroups128)) || g.nsel <= 64)
+        __syncthreads();  // the loads stay in flight across it
       LaneKeys lk;
       lk.nj = nj;
       lk.cached = true;
