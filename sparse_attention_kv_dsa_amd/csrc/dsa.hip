@@ -132,6 +132,44 @@ __device__ __forceinline__ uint32_t group_umax(uint32_t v) {
   return v;
 }
 
+// The vector path's reductions over G lanes: the same as group_max /
+// group_umax up to G = 16; beyond, the steps across rows go through DPP row
+// broadcasts (lane 15 of a row into the next row, lane 31 into rows 2 and 3)
+// instead of a swizzle and a bpermute, so the group's value is only whole in
+// its lane kTailLane<G> (the first lane of its last row).
+template <int G>
+constexpr int kTailLane = G >= 64 ? 48 : (G >= 32 ? 16 : 0);
+
+template <int G>
+__device__ __forceinline__ float group_max_tail(float v) {
+  if constexpr (G <= 16) {
+    return group_max<G>(v);
+  } else {
+    v = group_max<16>(v);
+    v = fmaximum(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                  __builtin_bit_cast(int, v),
+                                                  __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false)));
+    if constexpr (G >= 64)
+      v = fmaximum(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                    __builtin_bit_cast(int, v),
+                                                    __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false)));
+    return v;
+  }
+}
+
+template <int G>
+__device__ __forceinline__ uint32_t group_umax_tail(uint32_t v) {
+  if constexpr (G <= 16) {
+    return group_umax<G>(v);
+  } else {
+    v = group_umax<16>(v);
+    v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));
+    if constexpr (G >= 64)
+      v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));
+    return v;
+  }
+}
+
 // Streaming loads: each logit is read once, so the loads are nontemporal
 // (measured 1-12 % faster per workload on this chip than cached loads).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -301,22 +339,23 @@ __device__ __forceinline__ void stream_vec(const RowGeom& g, int32_t b0, int32_t
       const float m4 = fmaximum(fmaximum(x4.x, x4.y), fmaximum(x4.z, x4.w));
       m = cols == 4 ? m4 : (cols > 0 ? tail : ninf);
     }
-    if constexpr (Emit::kKey && G <= 16) {
+    if constexpr (Emit::kKey) {
       // emitters of keys: the group maximum taken on the keys, whose DPP
       // moves fold into the integer maximum (one instruction per step
       // instead of a move and a float maximum): large prefill 151.66 ->
       // 151.36 us, prefill chunk 13.48 -> 13.36, decode batch 6.94 -> 6.88;
-      // at G = 32 (a swizzle step too) the long-context decode lost 0.4 %
-      const uint32_t k = group_umax<G>(order_key(m));
+      // with the row broadcasts of group_umax_tail at G = 32, long-context
+      // decode 14.20 -> 13.80 (14.10 with them on floats)
+      const uint32_t k = group_umax_tail<G>(order_key(m));
       if (t < c.ntiles) {
         const int32_t b = b0 + (((t << 6) + lane) / G);
-        if ((lane % G) == 0 && b < b1) emit.key(b, k);
+        if ((lane % G) == kTailLane<G> && b < b1) emit.key(b, k);
       }
     } else {
-      m = group_max<G>(m);
+      m = group_max_tail<G>(m);
       if (t < c.ntiles) {
         const int32_t b = b0 + (((t << 6) + lane) / G);
-        if ((lane % G) == 0 && b < b1) emit(b, m);
+        if ((lane % G) == kTailLane<G> && b < b1) emit(b, m);
       }
     }
   };
