@@ -56,6 +56,11 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = 8;
+// The pair plan (one workgroup per CU, latency-bound) streams its parts with
+// 4 loads in flight per lane: decode batch 6.89 -> 6.34 us, long-context
+// decode 13.76 -> 13.45 against 8 (2, 3 and 6 were slower, 12 and 16 far
+// slower); the wave, group and block-score kernels lost 1-3 % at 4.
+constexpr int kPairUnroll = 4;
 
 constexpr size_t kLdsLimit = 65536;
 constexpr int64_t kMaxGrid = 1 << 20;
@@ -1320,7 +1325,7 @@ __global__ void __launch_bounds__(NW ? NW * 64 : 1024) select_pair_rows_kernel(P
   select_row_prepare(ctl, area, tid, nt);
   const int32_t b0 = part * cb < g.nvb ? part * cb : g.nvb;
   const int32_t b1 = b0 + cb < g.nvb ? b0 + cb : g.nvb;
-  stream_blocks<G, kUnroll, true, FULL>(p, g, b0, b1, wave, nw, EmitKey{smem});
+  stream_blocks<G, kPairUnroll, true, FULL>(p, g, b0, b1, wave, nw, EmitKey{smem});
   const int HP = g.nvb > 0 ? (g.nvb + cb - 1) / cb : 1;  // parts the row uses
   if (HP > 1) {  // workgroup-uniform; a row of one part needs no hand-off
     __syncthreads();
@@ -1360,8 +1365,8 @@ __global__ void __launch_bounds__(NW ? NW * 64 : 1024) select_pair_rows_kernel(P
         }
       }
     } else {
-      stream_blocks<G, kUnroll, true, FULL>(p, g, 0, b0, wave, nw, EmitKey{smem});
-      stream_blocks<G, kUnroll, true, FULL>(p, g, b1, g.nvb, wave, nw, EmitKey{smem});
+      stream_blocks<G, kPairUnroll, true, FULL>(p, g, 0, b0, wave, nw, EmitKey{smem});
+      stream_blocks<G, kPairUnroll, true, FULL>(p, g, b1, g.nvb, wave, nw, EmitKey{smem});
     }
   }
   __syncthreads();
