@@ -2056,28 +2056,36 @@ dsa_status_t dsa_select_plan(int64_t rows, int64_t width, int32_t block_size,
   *plan_arg = 0;
   if (rows >= 1024 || nchunks <= 1) {
     // Enough rows to fill the GPU one row at a time: short rows one wave
-    // each, long rows a whole workgroup each.
-    *plan = width <= 16384 ? kPlanWave : kPlanGroup;
+    // each, long rows a whole workgroup each.  Fewer rows of one chunk each
+    // (up to 8K-32K columns): four waves per row, except for rows of at most
+    // 2K columns (512 x 8192: 6.69 us against 8.92 for a wave per row;
+    // 128 x 2048: 5.15 against 4.98).
+    *plan = width <= 16384 && (rows >= 1024 || width <= 2048) ? kPlanWave : kPlanGroup;
     if (*plan == kPlanGroup) *plan_arg = kWaves;
-  } else if (rows <= 128 && width >= 32768) {
-    // Decode batches of up to 128 rows of 32K columns or more: 2-8
-    // workgroups share each row (the pair plan), so that every CU streams;
-    // it beat the one-workgroup-per-row and split plans on every such shape
-    // measured (8-128 rows, 32K-256K columns, block sizes 64 and 128).
+  } else if (rows <= kCountRows && width >= 16384 && (rows <= 128 || width <= 131072)) {
+    // Decode batches of up to 256 rows of 16K columns or more (up to 128K
+    // beyond 128 rows): 2-8 workgroups share each row (the pair plan), so
+    // that every CU streams.  It beat the one-workgroup-per-row and split
+    // plans on every such shape measured (8-256 rows, 16K-256K columns,
+    // block sizes 64 and 128; e.g. 64 x 16384: 5.78 us against 6.54 for
+    // four waves per row, 256 x 65536 at k = 64: 13.3 against 14.6); 192
+    // rows of 256K columns took 34.6 us against 28.0 split.
     int parts, waves;
     pair_shape(rows, width, &parts, &waves);
     *plan = kPlanPair;
     *plan_arg = waves | parts << 8;
   } else if (rows >= cdiv(width, 1024) || width <= 32768) {  // rows * 1024 >= width
     // Rows of up to 32K columns, or enough rows to keep HBM busy one CU per
-    // row (256 rows of 256K columns): 8 or 16 waves stream each row, the
+    // row (256 rows of 256K columns): 4-16 waves stream each row, the
     // select fused behind them in the same launch.  Measured against the
     // split plan's two kernels, the crossover sits near rows = width / 1024
-    // for block sizes 64 and 128; 8 waves beat 16 on rows of up to 32K
-    // columns (a shorter select, two load rounds each), 16 win from 64K
-    // columns on.
+    // for block sizes 64 and 128; four waves win on rows of up to 16K
+    // columns (512 x 16384: 8.59 us against 9.81 for eight), 8 beat 16 on
+    // rows of up to 32K columns (a shorter select, two load rounds each),
+    // 16 win from 64K columns on.
     *plan = kPlanGroup;
-    *plan_arg = rows <= 256 ? (width <= 32768 ? 8 : 16) : (rows <= 512 ? 8 : kWaves);
+    *plan_arg = width <= 16384 ? kWaves
+                               : (rows <= 256 ? (width <= 32768 ? 8 : 16) : (rows <= 512 ? 8 : kWaves));
   } else {
     // Few rows, or long rows: chunks of every row on all CUs, then a
     // selecting kernel (one CU streams only ~25-70 GB/s, so a row per CU

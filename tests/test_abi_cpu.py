@@ -66,8 +66,11 @@ def test_auto_plan():
     assert B.select_plan(4096, 16384, 64, 32) == (3, 0)    # many short rows: a wave per row
     assert B.select_plan(8192, 65536, 64, 64) == (1, 4)    # many long rows: a workgroup per row
     assert B.select_plan(8, 1000, 64, 4) == (3, 0)         # one chunk per row anyway
-    # decode batches of up to 128 rows of >= 32K columns: the pair plan,
-    # plan_arg = waves | parts << 8
+    # fewer rows of one chunk each: four waves per row (rows of <= 2K: a wave)
+    assert B.select_plan(512, 8192, 64, 32) == (1, 4)
+    assert B.select_plan(128, 2048, 64, 32) == (3, 0)
+    # decode batches of up to 256 rows of >= 16K columns (<= 128K columns
+    # beyond 128 rows): the pair plan, plan_arg = waves | parts << 8
     assert B.select_plan(64, 32768, 64, 32) == (4, 8 | 4 << 8)
     assert B.select_plan(64, 65536, 64, 32) == (4, 8 | 4 << 8)
     assert B.select_plan(64, 131072, 64, 32) == (4, 8 | 4 << 8)
@@ -77,10 +80,13 @@ def test_auto_plan():
     assert B.select_plan(96, 262144, 128, 16) == (4, 16 | 2 << 8)
     assert B.select_plan(16, 131072, 128, 16) == (4, 8 | 8 << 8)
     assert B.select_plan(1, 262144, 128, 16) == (4, 16 | 8 << 8)
-    # shorter rows: one workgroup per row, also for few rows
-    assert B.select_plan(8, 16384, 64, 32) == (1, 8)
-    assert B.select_plan(128, 16384, 64, 32) == (1, 8)
-    assert B.select_plan(192, 65536, 64, 32) == (1, 16)
+    assert B.select_plan(8, 16384, 64, 32) == (4, 8 | 2 << 8)
+    assert B.select_plan(128, 16384, 64, 32) == (4, 8 | 2 << 8)
+    assert B.select_plan(192, 65536, 64, 32) == (4, 8 | 2 << 8)
+    assert B.select_plan(256, 131072, 64, 32) == (4, 8 | 2 << 8)
+    # one workgroup per row: more rows, or rows too long for the pair plan
+    assert B.select_plan(512, 16384, 64, 32) == (1, 4)
+    assert B.select_plan(300, 32768, 64, 32) == (1, 8)
     assert B.select_plan(256, 262144, 64, 32) == (1, 16)
     assert B.select_plan(600, 131072, 128, 16) == (1, 4)
     assert B.select_plan(600, 32768, 64, 32) == (1, 4)
