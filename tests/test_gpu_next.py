@@ -91,6 +91,28 @@ def test_select_from_scores_full_size():
     assert np.array_equal(got, _oracle_sfs(w))
 
 
+def test_select_from_scores_repeats_identical():
+    """The two-wave rows of the full-size DCP share (no barrier between
+    clearing a row's select state and its select) give the oracle's ids on
+    every one of 12 back-to-back calls, at k = 64 (128 group maxima) and at
+    k = 32 (64 group maxima, the split rank)."""
+    base = workloads.dcp_prefill_scores()
+    for k in (64, 32):
+        w = workloads.ScoresWorkload(f"{base.name}-k{k}", base.scores, base.global_row_ke,
+                                     base.global_block_size, base.max_global_blocks, k,
+                                     base.row_repeat)
+        exp = _oracle_sfs(w)
+        sc = torch.from_numpy(w.scores).to(DEV)
+        ke = _i32(w.global_row_ke)
+        outs = [torch.empty((sc.shape[0], k), dtype=torch.int32, device=DEV) for _ in range(12)]
+        for o in outs:  # back to back on one stream
+            dsa.select_from_scores(sc, ke, k, w.global_block_size, w.max_global_blocks, o,
+                                   w.row_repeat)
+        torch.cuda.synchronize()
+        for i, o in enumerate(outs):
+            assert np.array_equal(o.cpu().numpy(), exp), (k, i)
+
+
 @pytest.mark.parametrize("rows,k", [(200, 7), (700, 64), (3000, 64), (3000, 300)])
 def test_select_from_scores_row_counts(rows, k):
     """The workgroup width follows the row count (16, 4 or 2 waves per row):
