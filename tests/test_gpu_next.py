@@ -237,6 +237,29 @@ def test_block_score_keys_random(pin):
         assert np.array_equal(_np_codes(got), exp), i
 
 
+@pytest.mark.parametrize("B", [4, 8, 16, 32, 64, 128, 256])
+def test_block_scores_every_vector_block_size(B):
+    """Every block size of the vector path (16 to 1024 bytes per block, one
+    to 64 lanes per block; from 128 on the lanes of a block span rows of 16
+    and combine through row broadcasts), as fp32 scores and as codes, pin on
+    and off, unaligned windows and starts, few rows (chunks) and many (whole
+    rows): bit-exact against the oracle."""
+    for seed, rows, width in ((B, 40, 9000 + B), (B + 1, 1030, 2 * B * 37 + 5)):
+        w = workloads.many_rows_case(900 + seed, rows, width, B, 1 + seed % 2)
+        x = torch.from_numpy(w.logits).to(DEV)
+        ks = None if w.row_ks is None else _i32(w.row_ks)
+        for pin in (True, False):
+            got = dsa.block_scores(x, ks, _i32(w.row_ke), B, w.row_repeat, pin_newest=pin)
+            exp = oracle.block_scores(w.logits, w.row_ks, w.row_ke, B, w.row_repeat,
+                                      pin_newest=pin, nthreads=HOST_THREADS)
+            assert np.array_equal(got.cpu().numpy().view(np.uint32), exp.view(np.uint32)), \
+                (B, rows, width, pin)
+            got = dsa.block_score_keys(x, ks, _i32(w.row_ke), B, w.row_repeat, pin_newest=pin)
+            exp = oracle.block_score_keys(w.logits, w.row_ks, w.row_ke, B, w.row_repeat,
+                                          pin_newest=pin, nthreads=HOST_THREADS)
+            assert np.array_equal(_np_codes(got), exp), (B, rows, width, pin, "codes")
+
+
 def test_block_score_keys_full_size():
     """One DCP rank's local scores at the benchmarked size as codes: every
     code of every row equals the oracle's."""
