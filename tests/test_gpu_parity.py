@@ -486,6 +486,33 @@ def test_pair_plan_leaves_counters_zero():
                 assert int(ws.buf[:2048].count_nonzero()) == 0, (w.name, hex(arg))
 
 
+@pytest.mark.parametrize("rows,width,B,k,R,starts", [
+    (8, 16384, 64, 32, 1, False), (200, 20000, 64, 32, 1, True), (256, 16384, 64, 64, 2, False),
+    (160, 131072, 128, 16, 2, True)])
+def test_auto_plan_pair_shapes(rows, width, B, k, R, starts):
+    """Shapes the automatic plan gives the pair plan (up to 256 rows of 16K
+    columns or more): run through the default plan with a workspace, every
+    row's ids and scores as the oracle's."""
+    assert dsa.select_plan(rows, width, B, k)[0] == 4
+    rng = np.random.default_rng(rows + width)
+    x = rng.standard_normal((rows, width)).astype(np.float32)
+    x[rng.random((rows, width)) < 1e-3] = -np.inf
+    groups = -(-rows // R)
+    ks = rng.integers(-B, width // 3, size=groups).astype(np.int32) if starts else None
+    ke = ((ks if starts else 0) + rng.integers(-5, width + B, size=groups)).astype(np.int32)
+    w = workloads.Workload(f"auto-pair-{rows}x{width}", x, ks, ke, B, k, R)
+    exp_out, exp_sc = oracle_select(w)
+    xd = dev_logits(x)
+    ws = dsa.Workspace(DEV, dsa.select_workspace_bytes(rows, width, B, k))
+    out = torch.full((rows, k), 7, dtype=torch.int32, device=DEV)
+    nb = -(-width // B)
+    sc = torch.full((rows, nb), 777.0, dtype=torch.float32, device=DEV)
+    dsa.select_candidate_blocks(xd, dev_i32(ks), dev_i32(ke), k, B, out, R, scores_out=sc,
+                                workspace=ws)
+    torch.cuda.synchronize()
+    assert_same(out.cpu().numpy(), sc.cpu().numpy(), exp_out, exp_sc, w.name)
+
+
 def test_two_streams_two_workspaces():
     wa, wb = workloads.config(2), workloads.config(4)
     exp_a, _ = oracle_select(wa)
