@@ -63,6 +63,7 @@ constexpr int kUnroll = 8;
 constexpr int kPairUnroll = 4;
 
 constexpr size_t kLdsLimit = 65536;
+constexpr size_t kGroupLdsThree = 160 * 1024 / 4 + 256;  // > 1/4 of a CU's LDS: three per CU
 constexpr int64_t kMaxGrid = 1 << 20;
 
 // Order-preserving keys: for non-NaN floats a < b  <=>  key(a) < key(b) as
@@ -544,7 +545,10 @@ __device__ __forceinline__ uint64_t cand_word(uint32_t rk, uint32_t i) {
 
 // Ranks cand[0, ncand) (distinct words, 0 = empty): slot r < keff of the
 // output takes the id of the word with r larger words.  Wave `wave` of `nw`
-// takes every nw-th group of 64 candidates.
+// takes every nw-th group of 64 candidates.  WIDE: runs of 16 words (eight
+// reads in flight, two independent sums) ahead of the runs of 8, a shorter
+// chain for kernels that can spare the registers.
+template <bool WIDE = false>
 __device__ __forceinline__ void rank_candidates(const uint64_t* cand, int32_t ncand, int32_t keff,
                                                 int32_t* out_row, int wave, int nw) {
   const int lane = threadIdx.x & 63;
@@ -554,6 +558,22 @@ __device__ __forceinline__ void rank_candidates(const uint64_t* cand, int32_t nc
     const uint64_t ci = idx < ncand ? cand[idx] : 0ull;
     uint32_t r = 0;
     int32_t j = 0;
+    if constexpr (WIDE) {
+      uint32_t r1 = 0;
+      for (; j + 16 <= ncand; j += 16) {
+        const ulonglong2 a = c2[(j >> 1) + 0], b = c2[(j >> 1) + 1];
+        const ulonglong2 c = c2[(j >> 1) + 2], d = c2[(j >> 1) + 3];
+        const ulonglong2 e = c2[(j >> 1) + 4], f = c2[(j >> 1) + 5];
+        const ulonglong2 g = c2[(j >> 1) + 6], h = c2[(j >> 1) + 7];
+        r += (uint32_t)(a.x > ci) + (uint32_t)(a.y > ci) + (uint32_t)(b.x > ci) +
+             (uint32_t)(b.y > ci) + (uint32_t)(c.x > ci) + (uint32_t)(c.y > ci) +
+             (uint32_t)(d.x > ci) + (uint32_t)(d.y > ci);
+        r1 += (uint32_t)(e.x > ci) + (uint32_t)(e.y > ci) + (uint32_t)(f.x > ci) +
+              (uint32_t)(f.y > ci) + (uint32_t)(g.x > ci) + (uint32_t)(g.y > ci) +
+              (uint32_t)(h.x > ci) + (uint32_t)(h.y > ci);
+      }
+      r += r1;
+    }
     for (; j + 8 <= ncand; j += 8) {  // broadcast reads, four in flight
       const ulonglong2 a = c2[(j >> 1) + 0], b = c2[(j >> 1) + 1];
       const ulonglong2 c = c2[(j >> 1) + 2], d = c2[(j >> 1) + 3];
@@ -922,11 +942,28 @@ __device__ __forceinline__ uint32_t maxima_bound(uint32_t g0, uint32_t g1, uint3
     }
   }
   if (ct > kq + (kq >> 2)) {  // wave-uniform
-    for (int bit = 15; bit >= 0; --bit) {
-      const uint32_t c = t | (1u << bit);
-      uint32_t cnt = (uint32_t)__popcll(__ballot(g0 >= c));
-      if constexpr (N == 2) cnt += (uint32_t)__popcll(__ballot(g1 >= c));
-      if (cnt >= kq) t = c;
+    // Fewer than kq maxima lie above the 2^16-code bucket [t, t + 2^16),
+    // so the kq-th largest lies in it: when every maximum in the bucket has
+    // one value (ties), that value is the exact bound and the 16 low steps
+    // are skipped.
+    const bool in0 = g0 >= t && g0 - t < 65536u;
+    uint32_t hi = in0 ? g0 : 0u, nlo = in0 ? ~g0 : 0u;
+    if constexpr (N == 2) {
+      const bool in1 = g1 >= t && g1 - t < 65536u;
+      hi = umax(hi, in1 ? g1 : 0u);
+      nlo = umax(nlo, in1 ? ~g1 : 0u);
+    }
+    hi = (uint32_t)__builtin_amdgcn_readlane((int)group_umax_tail<64>(hi), 63);
+    nlo = (uint32_t)__builtin_amdgcn_readlane((int)group_umax_tail<64>(nlo), 63);
+    if (hi == ~nlo) {  // wave-uniform
+      t = hi;
+    } else {
+      for (int bit = 15; bit >= 0; --bit) {
+        const uint32_t c = t | (1u << bit);
+        uint32_t cnt = (uint32_t)__popcll(__ballot(g0 >= c));
+        if constexpr (N == 2) cnt += (uint32_t)__popcll(__ballot(g1 >= c));
+        if (cnt >= kq) t = c;
+      }
     }
   }
   return t;
@@ -1111,7 +1148,7 @@ __device__ __forceinline__ void select_row_general(const Params& p, const RowGeo
     rank_candidates_split(cand, ncand, keff, out_row, area, wave, nw);
     for (int32_t j = keff + tid; j < k; j += nt) out_row[j] = -1;
   } else if (ncand <= kCandCap) {
-    rank_candidates(cand, ncand, keff, out_row, wave, nw);
+    rank_candidates<!PRE>(cand, ncand, keff, out_row, wave, nw);
     for (int32_t j = keff + tid; j < k; j += nt) out_row[j] = -1;
   } else {
     if constexpr (PRE) {  // the exact select reads the keys from LDS
@@ -2271,7 +2308,12 @@ dsa_status_t dsa_select_candidate_blocks_plan(
     const int waves = plan_arg > 0 ? plan_arg : kWaves;
     void* fn = select_group_fixed_ptr(g, waves, topk_blocks);
     if (!fn) fn = select_group_rows_kernel_ptr(g);
-    return launch(fn, rows, 64 * waves, 1, (size_t)ww * 4, stream, p);
+    // Many long rows: the LDS request holds a CU to three rows at a time
+    // (gfx950: 160 KiB of LDS per CU).  Large prefill 150.45 -> 148.8 us
+    // against the five that registers allow (four: 149.9; two: 171).
+    size_t lds = (size_t)ww * 4;
+    if (rows >= 1024 && waves == kWaves && lds < kGroupLdsThree) lds = kGroupLdsThree;
+    return launch(fn, rows, 64 * waves, 1, lds, stream, p);
   }
   if (plan == kPlanPair) {
     int parts, waves;
