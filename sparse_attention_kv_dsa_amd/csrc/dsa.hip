@@ -1240,8 +1240,8 @@ __global__ void __launch_bounds__(kThreads) select_wave_rows_kernel(Params p) {
 // Plan "group": all waves of a workgroup stream one row into LDS, then select
 // it together.  NW (wave count) and FB (bound) fixed at compile time, or 0 and
 // -1 for the launch's and k's: the fixed instances for the usual shapes hold
-// fewer registers (4 waves, block size 64: 112 -> 81 VGPRs, five waves per
-// SIMD instead of four).
+// fewer registers (4 waves, block size 64: 112 -> 85 VGPRs; from 1024 rows
+// the host holds a CU to three such workgroups through their LDS request).
 template <int G, int NW = 0, int FB = -1>
 __global__ void __launch_bounds__(NW ? NW * 64 : 1024) select_group_rows_kernel(Params p) {
   extern __shared__ uint32_t smem[];
