@@ -2111,18 +2111,26 @@ dsa_status_t dsa_select_plan(int64_t rows, int64_t width, int32_t block_size,
     pair_shape(rows, width, &parts, &waves);
     *plan = kPlanPair;
     *plan_arg = waves | parts << 8;
-  } else if (rows >= cdiv(width, 1024) || width <= 32768) {  // rows * 1024 >= width
+  } else if (rows >= cdiv(width, 1024) || width <= 32768 ||
+             (width <= 524288 && rows >= 224)) {
     // Rows of up to 32K columns, or enough rows to keep HBM busy one CU per
-    // row (256 rows of 256K columns): 4-16 waves stream each row, the
-    // select fused behind them in the same launch.  Measured against the
-    // split plan's two kernels, the crossover sits near rows = width / 1024
-    // for block sizes 64 and 128; four waves win on rows of up to 16K
-    // columns (512 x 16384: 8.59 us against 9.81 for eight), 8 beat 16 on
-    // rows of up to 32K columns (a shorter select, two load rounds each),
-    // 16 win from 64K columns on.
+    // row: 4-16 waves stream each row, the select fused behind them in the
+    // same launch.  Against the split plan's two kernels the crossover sits
+    // near 224 rows for rows of up to 512K columns (192 x 262144: 29.3 us
+    // against 27.7 split; 210 x 400000: 44.7 against 41.2; 224 x 524288:
+    // 55.0 against 58.7; 256 x 524288 at B = 128: 59.5 against 63.5) and
+    // near rows = width / 1024 beyond (300 x 1048576: 137.1 against 134.2).
+    // Waves per row by row length (the pair plan takes up to 256 rows of
+    // 16K-128K columns): 4 up to 16K columns (512 x 16384: 8.59 us against 9.81 for
+    // eight), 8 up to 32K below 512 rows, 4 at 64K (512 x 65536: 18.9
+    // against 19.9), 8 at 128K (600 x 131072: 34.7 against 41.7 for four),
+    // 16 beyond (320 x 262144: 43.6 against 51.2 for eight).
     *plan = kPlanGroup;
-    *plan_arg = width <= 16384 ? kWaves
-                               : (rows <= 256 ? (width <= 32768 ? 8 : 16) : (rows <= 512 ? 8 : kWaves));
+    *plan_arg = width <= 16384   ? kWaves
+                : width <= 32768 ? (rows <= 512 ? 8 : kWaves)
+                : width <= 65536 ? kWaves
+                : width <= 131072 ? 8
+                                  : 16;
   } else {
     // Few rows, or long rows: chunks of every row on all CUs, then a
     // selecting kernel (one CU streams only ~25-70 GB/s, so a row per CU

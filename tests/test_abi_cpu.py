@@ -88,7 +88,10 @@ def test_auto_plan():
     assert B.select_plan(512, 16384, 64, 32) == (1, 4)
     assert B.select_plan(300, 32768, 64, 32) == (1, 8)
     assert B.select_plan(256, 262144, 64, 32) == (1, 16)
-    assert B.select_plan(600, 131072, 128, 16) == (1, 4)
+    assert B.select_plan(600, 131072, 128, 16) == (1, 8)
+    assert B.select_plan(512, 65536, 64, 32) == (1, 4)
+    assert B.select_plan(320, 262144, 64, 32) == (1, 16)
+    assert B.select_plan(224, 524288, 64, 32) == (1, 16)
     assert B.select_plan(600, 32768, 64, 32) == (1, 4)
     # more than 128 rows, too few for their length: split
     assert B.select_plan(192, 262144, 64, 32) == (2, 384)
@@ -257,8 +260,9 @@ def test_noalloc_host_checks():
         return L.dsa_select_candidate_blocks_noalloc(FAKE, rows, width, ld or width, None, ke, k,
                                                      B_, 1, out, k, None, 0, None)
 
-    assert B.select_workspace_bytes(300, 448000, 32, 16) > 16 << 20
-    assert call(300, 448000, 32, 16) == 3            # the split plan's keys exceed the scratch
+    assert B.select_plan(300, 600000, 40, 16)[0] == 2
+    assert B.select_workspace_bytes(300, 600000, 40, 16) > 16 << 20
+    assert call(300, 600000, 40, 16) == 3            # the split plan's keys exceed the scratch
     assert call(-1, 100, 8, 4) == 1 and call(4, 100, 0, 4) == 1 and call(4, 100, 8, -1) == 1
     assert call(4, 100, 8, 4, ld=99) == 1 and call(4, 100, 8, 4, ke=None) == 1
     assert call(0, 100, 8, 4) == 0 and call(4, 100, 8, 0) == 0   # nothing to do

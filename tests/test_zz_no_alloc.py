@@ -75,13 +75,13 @@ def test_noalloc_pair_plan_twice_smaller_second():
 
 
 def test_noalloc_split_plan_twice_smaller_second():
-    for rows, width in ((200, 262144), (150, 200000)):
+    for rows, width in ((190, 262144), (150, 200000)):
         w = workloads.many_rows_case(77 + rows, rows, width, 64, 1, 32)
         _check(w)
 
 
 def test_noalloc_rejects_more_than_its_scratch():
-    rows, width, B, k = 300, 448000, 32, 16   # the split plan, 300 x 14016 keys > 16 MiB
+    rows, width, B, k = 300, 600000, 40, 16   # the split plan, 300 x 15008 keys > 16 MiB
     assert dsa.select_plan(rows, width, B, k)[0] == 2
     assert dsa.select_workspace_bytes(rows, width, B, k) > SCRATCH_BYTES
     x = torch.zeros((rows, width), dtype=torch.float32, device=DEV)
