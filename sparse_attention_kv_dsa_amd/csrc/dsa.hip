@@ -2097,8 +2097,11 @@ dsa_status_t dsa_select_plan(int64_t rows, int64_t width, int32_t block_size,
     // (up to 8K-32K columns): four waves per row, except for rows of at most
     // 2K columns (512 x 8192: 6.69 us against 8.92 for a wave per row;
     // 128 x 2048: 5.15 against 4.98).
+    // Many rows of 128K columns or more: eight waves per row (2048 x 131072
+    // at B = 128: 88.6 us against 94.9 for four; 1024 x 262144: 101.4
+    // against 102.4; sixteen were slower).
     *plan = width <= 16384 && (rows >= 1024 || width <= 2048) ? kPlanWave : kPlanGroup;
-    if (*plan == kPlanGroup) *plan_arg = kWaves;
+    if (*plan == kPlanGroup) *plan_arg = rows >= 1024 && width >= 131072 ? 8 : kWaves;
   } else if (rows <= kCountRows && width >= 16384 && (rows <= 128 || width <= 131072)) {
     // Decode batches of up to 256 rows of 16K columns or more (up to 128K
     // beyond 128 rows): 2-8 workgroups share each row (the pair plan), so

@@ -65,6 +65,7 @@ def test_workspace_bytes():
 def test_auto_plan():
     assert B.select_plan(4096, 16384, 64, 32) == (3, 0)    # many short rows: a wave per row
     assert B.select_plan(8192, 65536, 64, 64) == (1, 4)    # many long rows: a workgroup per row
+    assert B.select_plan(2048, 131072, 128, 32) == (1, 8)  # longer rows: eight waves each
     assert B.select_plan(8, 1000, 64, 4) == (3, 0)         # one chunk per row anyway
     # fewer rows of one chunk each: four waves per row (rows of <= 2K: a wave)
     assert B.select_plan(512, 8192, 64, 32) == (1, 4)
