@@ -1240,7 +1240,7 @@ __global__ void __launch_bounds__(kThreads) select_wave_rows_kernel(Params p) {
 // Plan "group": all waves of a workgroup stream one row into LDS, then select
 // it together.  NW (wave count) and FB (bound) fixed at compile time, or 0 and
 // -1 for the launch's and k's: the fixed instances for the usual shapes hold
-// fewer registers (4 waves, block size 64: 112 -> 85 VGPRs; from 1024 rows
+// fewer registers (4 waves, block size 64: 112 -> 85 VGPRs; from 6144 rows
 // the host holds a CU to three such workgroups through their LDS request).
 template <int G, int NW = 0, int FB = -1>
 __global__ void __launch_bounds__(NW ? NW * 64 : 1024) select_group_rows_kernel(Params p) {
@@ -2319,11 +2319,14 @@ dsa_status_t dsa_select_candidate_blocks_plan(
     const int waves = plan_arg > 0 ? plan_arg : kWaves;
     void* fn = select_group_fixed_ptr(g, waves, topk_blocks);
     if (!fn) fn = select_group_rows_kernel_ptr(g);
-    // Many long rows: the LDS request holds a CU to three rows at a time
-    // (gfx950: 160 KiB of LDS per CU).  Large prefill 150.45 -> 148.8 us
-    // against the five that registers allow (four: 149.9; two: 171).
+    // Many long rows (24 or more per CU): the LDS request holds a CU to three
+    // rows at a time (gfx950: 160 KiB of LDS per CU).  Large prefill 150.45
+    // -> 148.8 us against the five that registers allow (four: 149.9; two:
+    // 171), 6144 x 65536 180.1 -> 176.5, 8192 x 32768 120.6 -> 119.9; with
+    // fewer rows per CU the extra rounds of rows cost more (1024 x 65536
+    // 39.4 -> 40.7, 4096 x 24576 50.7 -> 55.8), so they keep five.
     size_t lds = (size_t)ww * 4;
-    if (rows >= 1024 && waves == kWaves && lds < kGroupLdsThree) lds = kGroupLdsThree;
+    if (rows >= 6144 && waves == kWaves && lds < kGroupLdsThree) lds = kGroupLdsThree;
     return launch(fn, rows, 64 * waves, 1, lds, stream, p);
   }
   if (plan == kPlanPair) {
