@@ -608,7 +608,8 @@ def bench_select(cfg, args, dev, use_graph):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_for(w.name, plan),
                      "algorithmic_bytes_per_launch": alg, "in_window_bytes": win,
-                     "timed": "whole step (both kernels under the split plan)",
+                     "timed": ("whole step (both kernels of the split plan)" if plan == 2
+                               else "whole step (one kernel launch)"),
                      "kernel": KERNELS[plan]},
     }
     return res, w
