@@ -667,6 +667,64 @@ def test_select_at_lds_limit(plan):
         assert_same(got, sc, exp_out, exp_sc, f"lds limit k={k} plan {plan}")
 
 
+def test_rows_past_4_gib():
+    """Row offsets past 2^32 bytes: 72 rows 64 MB apart (4.6 GB of logits,
+    NaN after each row's first 6000 columns), so the last rows start beyond
+    4 GiB.  Every plan on an aligned base (16-byte loads) and an unaligned
+    one (scalar loads), against the oracle on every row; then the block
+    scores, the selection from scores and from codes (the rows' first 1000
+    columns) and the mask on the same rows, the mask leaving the NaN gaps
+    between the rows untouched."""
+    rng = np.random.default_rng(44)
+    rows, width, B, k, R = 72, 6000, 64, 24, 2
+    ld = 16_000_000
+    assert (rows - 3) * ld * 4 > 2 ** 32
+    groups = rows // R
+    x = (np.rint(rng.standard_normal((rows, width)) * 4) / 4).astype(np.float32)
+    x[rng.random((rows, width)) < 1e-3] = np.nan
+    ks = np.where(np.arange(groups) % 3 == 0, 0,
+                  rng.integers(-5, width // 2, size=groups)).astype(np.int32)
+    ke = np.clip(ks + rng.integers(-10, width + 40, size=groups), -3, width + 9).astype(np.int32)
+    w = workloads.Workload("past-4gib", x, ks, ke, B, k, R)
+    exp_out, exp_sc = oracle_select(w)
+    for offset in (0, 1):
+        for plan in (1, 2, 3, 4):
+            _say(f"rows past 4 GiB: base offset {offset}, plan {plan}")
+            got, sc = gpu_select(w, plan, 0, ld_pad=ld - width, offset=offset)
+            assert_same(got, sc, exp_out, exp_sc, f"past 4 GiB offset {offset} plan {plan}")
+    _say("rows past 4 GiB: block scores")
+    xd = dev_logits(x, ld - width)
+    got = dsa.block_scores(xd, dev_i32(ks), dev_i32(ke), B, R, pin_newest=True)
+    exp = oracle.block_scores(x, ks, ke, B, R, pin_newest=True, nthreads=HOST_THREADS)
+    assert np.array_equal(got.cpu().numpy().view(np.uint32), exp.view(np.uint32))
+    _say("rows past 4 GiB: select from scores, from keys")
+    nscore, gB = 1000, 64  # the rows' first 1000 columns as reduced scores / raw codes
+    gke = (ke.astype(np.int64) * 10).astype(np.int32)
+    for keys in (False, True):
+        o = torch.full((rows, k), 12345, dtype=torch.int32, device=DEV)
+        e = np.empty((rows, k), np.int32)
+        if keys:
+            dsa.select_from_keys(xd[:, :nscore].view(torch.int32), dev_i32(gke), k, gB, nscore,
+                                 o, R)
+            oracle.select_from_keys(np.ascontiguousarray(x[:, :nscore]).view(np.uint32), gke, k,
+                                    gB, nscore, e, R)
+        else:
+            dsa.select_from_scores(xd[:, :nscore], dev_i32(gke), k, gB, nscore, o, R)
+            oracle.select_from_scores(np.ascontiguousarray(x[:, :nscore]), gke, k, gB, nscore,
+                                      e, R)
+        torch.cuda.synchronize()
+        assert np.array_equal(o.cpu().numpy(), e), f"select from {'keys' if keys else 'scores'}"
+    _say("rows past 4 GiB: mask")
+    dsa.mask_candidates(xd, dev_i32(ks), dev_i32(ke), torch.from_numpy(exp_out).to(DEV),
+                        k, B, R)
+    torch.cuda.synchronize()
+    exp_m = x.copy()
+    oracle.mask_candidates(exp_m, ks, ke, exp_out, k, B, R)
+    assert np.array_equal(xd.cpu().numpy().view(np.uint32), exp_m.view(np.uint32))
+    gaps = xd.as_strided((rows, ld - width), (ld, 1), xd.storage_offset() + width)
+    assert bool(torch.isnan(gaps).all())
+
+
 def test_more_rows_than_one_grid():
     """More work items than one launch's grid (2^20 workgroups): the kernels
     stride over the rest.  1.1M short rows, grouped 3 to a bound."""
