@@ -116,7 +116,8 @@ dsa_status_t dsa_block_score_keys(const float* logits, int64_t rows, int64_t wid
  * dsa_select_candidate_blocks need for this shape: 2048 bytes of per-row
  * arrival counters (pair plan, up to 256 rows), then one uint32 score key
  * per row and block, rows padded to 32 keys.  Enough for every plan.  Pure
- * host arithmetic; returns 0 for invalid or empty shapes.
+ * host arithmetic; returns 0 for invalid or empty shapes and for shapes no
+ * plan holds (see Unsupported under dsa_select_candidate_blocks).
  */
 size_t dsa_select_workspace_bytes(int64_t rows, int64_t width, int32_t block_size,
                                   int32_t topk_blocks);
@@ -154,9 +155,17 @@ size_t dsa_select_workspace_bytes(int64_t rows, int64_t width, int32_t block_siz
  *   ld_logits < width, ld_out < topk_blocks, ld_scores < nblocks when
  *   scores_out is given, null logits/row_ke/out when there is work,
  *   misaligned pointers.
- * Unsupported: 4 * (roundup4(nblocks) + 48 + roundup4(max(1024, 2*kcap))) > 65536
- *   with kcap = max(1, min(topk_blocks, nblocks)) (a row's block scores and
- *   select scratch must fit in LDS), or more than 2^31 - 1 rows.
+ * Rows past LDS: when 4 * (roundup4(nblocks) + 48 + roundup4(max(1024,
+ *   2*kcap))) > 65536, with kcap = max(1, min(topk_blocks, nblocks)) (a
+ *   row's keys and select state exceed one workgroup's 64 KiB of LDS), only
+ *   the split plan holds the rows: its select reads the keys from the
+ *   workspace instead of LDS (correct, not tuned: every pass over the keys
+ *   reads HBM or L2).  The automatic plan takes it, and returns
+ *   DSA_ERR_WORKSPACE when the workspace is missing or too small.
+ * Unsupported: 4 * (48 + roundup4(max(1024, 2*kcap))) > 65536 (the select
+ *   state alone exceeds LDS, topk_blocks above 8168), rows past LDS under a
+ *   plan other than the split plan, more than 2^31 - 1 rows or blocks, or a
+ *   workspace size past size_t.
  */
 dsa_status_t dsa_select_candidate_blocks(const float* logits, int64_t rows, int64_t width,
                                          int64_t ld_logits, const int32_t* row_ks,
@@ -209,7 +218,9 @@ dsa_status_t dsa_select_candidate_blocks_noalloc(const float* logits, int64_t ro
  *                    select it together);
  *                 2: split: a first kernel streams chunks of `plan_arg`
  *                    blocks of every row on many CUs into the workspace as
- *                    keys, a second kernel selects, one workgroup per row;
+ *                    keys, a second kernel selects, one workgroup per row
+ *                    (reading the keys into LDS, or, for rows past LDS,
+ *                    straight from the workspace);
  *                 3: one wave per row (stream and select), several rows per
  *                    workgroup;
  *                 4: pair: several workgroups share a row, each streaming a

@@ -1315,6 +1315,32 @@ __global__ void __launch_bounds__(1024) select_keys_kernel(Params p) {
   }
 }
 
+// Plan "split", second kernel for rows whose keys exceed one workgroup's
+// LDS: the select reads the keys where the first kernel left them (the row
+// of the workspace) and keeps only its control words and candidate area in
+// LDS.  The keys past the window ([nvb, nsel)) and the pin are first written
+// into that row, as the exact fallback expects them in place; nothing else
+// reads or writes the row during the call.  Every pass over the keys reads
+// HBM or L2 instead of LDS: correct for any width, not tuned.
+__global__ void __launch_bounds__(1024) select_keys_hbm_kernel(Params p) {
+  extern __shared__ uint32_t smem[];
+  const int wave = wave_index();
+  const int nw = blockDim.x >> 6;
+  uint32_t* ctl = smem;
+  uint32_t* area = ctl + kCtlWords;
+  for (int64_t r = blockIdx.x; r < p.items; r += gridDim.x) {
+    const RowGeom g = row_geom(p, r, true);
+    uint32_t* keys = p.ws_keys + r * p.ws_ld;  // nsel <= nblocks <= ws_ld words
+    select_row_prepare(ctl, area, threadIdx.x, blockDim.x);
+    for (int32_t b = g.nvb + (int32_t)threadIdx.x; b < g.nsel; b += (int32_t)blockDim.x)
+      keys[b] = b == g.pin ? kKeyPosInf : kKeyNegInf;
+    if (threadIdx.x == 0 && g.pin >= 0 && g.pin < g.nvb) keys[g.pin] = kKeyPosInf;
+    __syncthreads();  // the workgroup's stores are visible to its loads after it
+    select_row<true>(p, r, g, keys, ctl, area, wave, nw);
+    if (r + gridDim.x < p.items) __syncthreads();
+  }
+}
+
 // Plan "pair": up to `parts` workgroups share a row.  Each streams one range
 // of the row's blocks (a fixed number of 32-block key lines) into LDS,
 // publishes its keys in the workspace and counts itself in on the row's
@@ -1972,10 +1998,21 @@ int64_t select_kcap(int64_t nblocks, int32_t k) {
 // the selected keys and ids (2 x kcap); a multiple of 4 words.
 int64_t select_keys_words(int64_t nblocks) { return cdiv(nblocks, 4) * 4; }
 
-int64_t select_wave_words(int64_t nblocks, int32_t k) {
+// The select state without the keys: control words and area.
+int64_t select_state_words(int64_t nblocks, int32_t k) {
   const int64_t sel = 2 * select_kcap(nblocks, k);
-  return select_keys_words(nblocks) + kCtlWords +
-         cdiv(sel > kAreaMinWords ? sel : kAreaMinWords, 4) * 4;
+  return kCtlWords + cdiv(sel > kAreaMinWords ? sel : kAreaMinWords, 4) * 4;
+}
+
+int64_t select_wave_words(int64_t nblocks, int32_t k) {
+  return select_keys_words(nblocks) + select_state_words(nblocks, k);
+}
+
+// Rows whose keys and select state exceed one workgroup's LDS: only the
+// split plan holds them, its select reading the keys from the workspace.
+bool keys_past_lds(int64_t nblocks, int32_t k) {
+  // the first test keeps the product below from overflowing for any nblocks
+  return nblocks > (int64_t)kLdsLimit / 4 || select_wave_words(nblocks, k) * 4 > (int64_t)kLdsLimit;
 }
 
 // Plan ids (also the values of dsa_select_candidate_blocks_plan's `plan`).
@@ -2078,8 +2115,11 @@ size_t dsa_select_workspace_bytes(int64_t rows, int64_t width, int32_t block_siz
                                   int32_t topk_blocks) {
   if (rows <= 0 || width <= 0 || block_size < 1 || topk_blocks < 0) return 0;
   const int64_t nblocks = cdiv(width, block_size);
-  // shapes no plan holds (a row's keys must fit in LDS): nothing to size
-  if (rows > INT32_MAX || nblocks > (int64_t)kLdsLimit / 4) return 0;
+  // shapes no plan holds (a row's select state past LDS even with its keys in
+  // the workspace): nothing to size
+  if (rows > INT32_MAX || nblocks > INT32_MAX) return 0;
+  if (select_state_words(nblocks, topk_blocks) * 4 > (int64_t)kLdsLimit) return 0;
+  if ((uint64_t)ws_row_words(nblocks) > (UINT64_MAX / 8u) / (uint64_t)rows) return 0;  // no size_t
   return kCountBytes + (size_t)rows * (size_t)ws_row_words(nblocks) * 4u;
 }
 
@@ -2091,7 +2131,9 @@ dsa_status_t dsa_select_plan(int64_t rows, int64_t width, int32_t block_size,
   const int32_t cb = auto_chunk_blocks(rows, width, block_size);
   const int64_t nchunks = cdiv(nblocks, cb);
   *plan_arg = 0;
-  if (rows >= 1024 || nchunks <= 1) {
+  if (keys_past_lds(nblocks, topk_blocks)) {
+    *plan = kPlanSplit;  // the only plan for rows whose keys exceed LDS
+  } else if (rows >= 1024 || nchunks <= 1) {
     // Enough rows to fill the GPU one row at a time: short rows one wave
     // each, long rows a whole workgroup each.  Fewer rows of one chunk each
     // (up to 8K-32K columns): four waves per row, except for rows of at most
@@ -2260,20 +2302,26 @@ dsa_status_t dsa_select_candidate_blocks_plan(
   if (!logits || !row_ke) return DSA_ERR_INVALID_ARG;
   if (misaligned(logits, 4) || (scores_out && misaligned(scores_out, 4)))
     return DSA_ERR_INVALID_ARG;
-  if (nblocks > (int64_t)kLdsLimit / 4) return DSA_ERR_UNSUPPORTED;  // keys alone exceed LDS
+  if (nblocks > INT32_MAX) return DSA_ERR_UNSUPPORTED;
   const int64_t ww = select_wave_words(nblocks, topk_blocks);
-  if (ww * 4 > (int64_t)kLdsLimit) return DSA_ERR_UNSUPPORTED;
+  // keys past LDS: the split plan with its keys left in the workspace
+  const bool hbm_keys = keys_past_lds(nblocks, topk_blocks);
+  if (select_state_words(nblocks, topk_blocks) * 4 > (int64_t)kLdsLimit)
+    return DSA_ERR_UNSUPPORTED;  // the select state alone exceeds LDS
 
   const size_t ws_need = dsa_select_workspace_bytes(rows, width, block_size, topk_blocks);
+  if (ws_need == 0) return DSA_ERR_UNSUPPORTED;  // a workspace past any size_t
   const bool ws_ok = workspace && workspace_bytes >= ws_need && !misaligned(workspace, kWsAlign);
   if (plan == 0) {
     dsa_select_plan(rows, width, block_size, topk_blocks, &plan, &plan_arg);
     if ((plan == kPlanSplit || plan == kPlanPair) && !ws_ok) {
+      if (hbm_keys) return DSA_ERR_WORKSPACE;  // no plan without one holds these rows
       // no usable workspace: the plan that needs none
       plan = kPlanGroup;
       plan_arg = width <= 32768 ? 8 : 16;
     }
   }
+  if (hbm_keys && plan != kPlanSplit) return DSA_ERR_UNSUPPORTED;
   if (plan == kPlanSplit && plan_arg == 0) plan_arg = auto_chunk_blocks(rows, width, block_size);
   if (plan == kPlanPair && rows > kCountRows) return DSA_ERR_UNSUPPORTED;
   if ((plan == kPlanSplit || plan == kPlanPair) && !ws_ok) return DSA_ERR_WORKSPACE;
@@ -2351,6 +2399,11 @@ dsa_status_t dsa_select_candidate_blocks_plan(
   if (rows * (int64_t)p.nchunks > (int64_t)INT32_MAX) return DSA_ERR_UNSUPPORTED;
   dsa_status_t st = launch(stream_keys_kernel_ptr(g), rows * p.nchunks, kThreads, 1, 0, stream, p);
   if (st != DSA_OK) return st;
+  if (hbm_keys) {  // 16 waves per row; LDS holds the select state only
+    p.keys_words = 0;
+    return launch(reinterpret_cast<void*>(&select_keys_hbm_kernel), rows, 1024, 1,
+                  (size_t)select_state_words(nblocks, topk_blocks) * 4, stream, p);
+  }
   // one workgroup per row, one key per thread up to 1024 keys
   int64_t sel_waves = cdiv(nblocks, 64);
   if (sel_waves > 16) sel_waves = 16;

@@ -11,6 +11,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from sparse_attention_kv_dsa_amd import build as dsa_build
 from sparse_attention_kv_dsa_amd import _binding as B
@@ -60,6 +61,10 @@ def test_workspace_bytes():
     assert L.dsa_select_workspace_bytes(5, 0, 7, 3) == 0
     assert L.dsa_select_workspace_bytes(5, 100, 0, 3) == 0
     assert L.dsa_select_workspace_bytes(5, 100, 4, -1) == 0
+    # rows past LDS (the split plan reads their keys from the workspace)
+    assert L.dsa_select_workspace_bytes(2, 1 << 20, 16, 32) == 2048 + 2 * 65536 * 4
+    assert L.dsa_select_workspace_bytes(2, 1 << 20, 1, 8200) == 0   # select state past LDS
+    assert L.dsa_select_workspace_bytes(1 << 30, 1 << 40, 1, 4) == 0  # past any size_t
 
 
 def test_auto_plan():
@@ -98,6 +103,10 @@ def test_auto_plan():
     assert B.select_plan(192, 262144, 64, 32) == (2, 384)
     p, cb = B.select_plan(300, 1 << 20, 128, 16)
     assert p == 2 and cb % 2 == 0 and cb >= 1
+    # rows past LDS, however few or many: split
+    assert B.select_plan(4, 15312 * 4 + 4, 4, 3)[0] == 2
+    assert B.select_plan(64, 1 << 20, 16, 32)[0] == 2
+    assert B.select_plan(4096, 1 << 20, 8, 2048)[0] == 2
 
 
 def _sel(**kw):
@@ -123,15 +132,36 @@ def _sel(**kw):
     (dict(plan=4, ws=None), 3),
     (dict(plan=4, ws_bytes=2047), 3), (dict(plan=4, ws=FAKE + 64), 3),
     (dict(plan=4, rows=257), 2),                                     # 256 arrival counters
-    (dict(width=1 << 20, ld=1 << 20, B=16, k=4096, ld_out=4096), 2),  # keys do not fit in LDS
-    (dict(width=15312 * 4 + 4, ld=1 << 16, B=4, k=3, ld_out=3), 2),   # 15316 + 48 + 1024 words > 16384
+    # keys past LDS: only the split plan, and only with its workspace (here
+    # 2048 + 4 * 65536 * 4 bytes, more than the 1 MiB given)
+    (dict(width=1 << 20, ld=1 << 20, B=16, k=4096, ld_out=4096), 3),
+    (dict(width=1 << 20, ld=1 << 20, B=16, k=4096, ld_out=4096, plan=1), 2),
+    (dict(width=1 << 20, ld=1 << 20, B=16, k=4096, ld_out=4096, plan=4), 2),
+    (dict(width=15312 * 4 + 4, ld=1 << 16, B=4, k=3, ld_out=3, plan=3), 2),  # 15316 + 48 + 1024 > 16384
+    (dict(width=15312 * 4 + 4, ld=1 << 16, B=4, k=3, ld_out=3, plan=2, ws=None), 3),
     (dict(width=15312 * 4, ld=1 << 16, B=4, k=3, ld_out=3, plan=2, ws=None), 3),  # 15312 + 48 + 1024 fits
+    # the select state alone past LDS: 48 + 16400 words
+    (dict(width=1 << 20, ld=1 << 20, B=1, k=8200, ld_out=8200, ws_bytes=1 << 30), 2),
     (dict(rows=0), 0), (dict(k=0), 0), (dict(rows=0, logits=None, ke=None, out=None), 0),
 ])
 def test_select_rejects_on_host(kw, code):
     assert _sel(**kw) == code
 
 
+@pytest.mark.skipif(torch.cuda.device_count() > 0,
+                    reason="reaches a kernel launch with placeholder pointers: host-only check")
+def test_rows_past_lds_reach_the_launch():
+    """Rows past LDS pass every host check under the automatic and the split
+    plan when the workspace holds their keys (DSA_ERR_HIP = 4 here, with no
+    GPU)."""
+    shape = dict(width=15312 * 4 + 4, ld=1 << 16, B=4, k=3, ld_out=3)
+    assert _sel(**shape) == 4 and _sel(**shape, plan=2) == 4 and _sel(**shape, plan=2, cb=7) == 4
+    big = dict(width=1 << 20, ld=1 << 20, B=16, k=4096, ld_out=4096, ws_bytes=(1 << 20) + 2048)
+    assert _sel(**big) == 4
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0,
+                    reason="reaches a kernel launch with placeholder pointers: host-only check")
 def test_auto_plan_without_workspace_takes_the_group_plan():
     """A pair-plan shape with no (or a too small or misaligned) workspace is
     not rejected under the automatic plan: it passes every host check and

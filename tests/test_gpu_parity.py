@@ -429,8 +429,12 @@ def test_errors_write_nothing():
         dsa.select_candidate_blocks(x, None, ke, 5, 8, out)   # ld_out < topk
     assert e.value.code == 1
     big = torch.ones((1, 1 << 16), device=DEV)
-    with pytest.raises(dsa.DsaError) as e:                    # 16384 keys + scratch exceed LDS
-        dsa.select_candidate_blocks(big, None, ke[:1], 4, 4, out[:1])
+    outb = torch.full((1, 8200), 7, dtype=torch.int32, device=DEV)
+    with pytest.raises(dsa.DsaError) as e:  # 16384 keys past LDS: only the split plan holds them
+        dsa.select_candidate_blocks(big, None, ke[:1], 4, 4, outb, plan=1)
+    assert e.value.code == 2
+    with pytest.raises(dsa.DsaError) as e:  # k = 8200: the select state alone exceeds LDS
+        dsa.select_candidate_blocks(big, None, ke[:1], 8200, 4, outb)
     assert e.value.code == 2
     ws = dsa.Workspace(DEV, 64)
     lib = dsa.lib()
@@ -439,7 +443,7 @@ def test_errors_write_nothing():
                                                 64, 2, 0, torch.cuda.current_stream().cuda_stream)
     assert code == 3   # the split plan needs 4 * 8 keys * 4 bytes
     torch.cuda.synchronize()
-    assert (out == 7).all()
+    assert (out == 7).all() and (outb == 7).all()
 
 
 def test_repeat_calls_bit_identical():
@@ -653,7 +657,7 @@ def test_candidate_counts_around_one_wave(plan):
 def test_select_at_lds_limit(plan):
     """The largest row the LDS holds: 15312 blocks (15312 keys + 48 control
     words + 1024 words of select area = 16384 words = 64 KiB); one block more
-    is rejected on the host (see test_abi_cpu)."""
+    takes the split plan's select from the workspace (test_rows_past_lds)."""
     rng = np.random.default_rng(plan)
     nb, B, rows = 15312, 4, 3
     width = nb * B
@@ -665,6 +669,43 @@ def test_select_at_lds_limit(plan):
         got, sc = gpu_select(w, plan, {2: 1000, 4: 3}.get(plan, 0))
         exp_out, exp_sc = oracle_select(w)
         assert_same(got, sc, exp_out, exp_sc, f"lds limit k={k} plan {plan}")
+
+
+@pytest.mark.parametrize("plan", [0, 2])
+def test_rows_past_lds(plan):
+    """Rows whose keys exceed LDS (the split plan, its select reading the
+    keys from the workspace): one block past the limit, 65536 blocks, and
+    token-level blocks (B = 1, 131072 columns, k = 2048); bounds by group
+    maxima, by radix and the exact fallback (k > 256, all-equal rows), ties,
+    NaN, windows with and without starts; ids and scores against the
+    oracle.  Then the allocation-free entry point on the same rows."""
+    rng = np.random.default_rng(60 + plan)
+    cases = [(6, 15313 * 4, 4, (3, 64, 200, 300)), (4, 1 << 20, 16, (32, 64)),
+             (2, 131072, 1, (2048,))]
+    for rows, width, B, ks_k in cases:
+        x = (np.rint(rng.standard_normal((rows, width)) * 8) / 8).astype(np.float32)
+        x[0, ::997] = np.nan
+        x[rows - 1] = np.float32(0.5)  # all equal: the bound admits every block
+        R = 2
+        g = rows // R
+        starts = [None, rng.integers(0, width // 8, size=g).astype(np.int32)]
+        for j, ks in enumerate(starts):
+            base = np.zeros(g, np.int64) if ks is None else ks.astype(np.int64)
+            ke = np.minimum(base + rng.integers(width // 2, width + 1, size=g),
+                            width + 3).astype(np.int32)
+            for k in ks_k:
+                w = workloads.Workload(f"past-lds-{width}-{B}-k{k}", x, ks, ke, B, k, R)
+                _say(f"rows past LDS: {rows} x {width}, B {B}, k {k}, starts {j}, plan {plan}")
+                got, sc = gpu_select(w, plan, 0 if plan == 0 else 1 + j * 999)
+                exp_out, exp_sc = oracle_select(w)
+                assert_same(got, sc, exp_out, exp_sc, f"past LDS {w.describe()} plan {plan}")
+        if plan == 0:
+            w = workloads.Workload(f"past-lds-noalloc-{width}", x, None, ke, B, ks_k[0], R)
+            o = torch.full((rows, ks_k[0]), 12345, dtype=torch.int32, device=DEV)
+            dsa.select_candidate_blocks_noalloc(torch.from_numpy(x).to(DEV), None, dev_i32(ke),
+                                                ks_k[0], B, o, R)
+            torch.cuda.synchronize()
+            assert np.array_equal(o.cpu().numpy(), oracle_select(w)[0])
 
 
 def test_rows_past_4_gib():
