@@ -164,8 +164,8 @@ size_t dsa_select_workspace_bytes(int64_t rows, int64_t width, int32_t block_siz
  *   DSA_ERR_WORKSPACE when the workspace is missing or too small.
  * Unsupported: 4 * (48 + roundup4(max(1024, 2*kcap))) > 65536 (the select
  *   state alone exceeds LDS, topk_blocks above 8168), rows past LDS under a
- *   plan other than the split plan, more than 2^31 - 1 rows or blocks, or a
- *   workspace size past size_t.
+ *   plan other than the split plan, more than 2^31 - 1 rows or
+ *   2^31 - 8193 blocks, or a workspace size past size_t.
  */
 dsa_status_t dsa_select_candidate_blocks(const float* logits, int64_t rows, int64_t width,
                                          int64_t ld_logits, const int32_t* row_ks,

@@ -632,6 +632,25 @@ __device__ __forceinline__ void rank_candidates_split(const uint64_t* cand, int3
 // Radix select (8-bit digits from the top) over the LDS rank keys of one
 // wave's slot array (slot j of lane l is key j*64 + l): the selection is every
 // key >= tg, then the first need_eq keys equal to T in id order.
+// Rank keys of slots [j, j + 8) of one wave's key array (slot j of lane l is
+// key j*64 + l), 0 past nsel, all eight loads issued before any is used: for
+// keys in HBM, where one load per step would wait out its whole latency.
+// nsel >= 1 (keys[0] is read in place of the slots past it).
+__device__ __forceinline__ void hbm_keys8(const uint32_t* keys, int32_t nsel, int32_t j,
+                                          uint32_t (&kv)[8]) {
+  const int lane = threadIdx.x & 63;
+  uint32_t raw[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int32_t i = (j + q) * 64 + lane;
+    raw[q] = keys[i < nsel ? i : 0];
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) kv[q] = (j + q) * 64 + lane < nsel ? rank_key(raw[q]) : 0u;
+}
+
+// HK: the keys sit in HBM (eight loads in flight per step), else in LDS.
+template <bool HK = false>
 __device__ void threshold_radix_lds(const uint32_t* keys, int32_t nsel, uint32_t keff,
                                     uint32_t* hist, uint32_t& tg, uint32_t& T, int32_t& need_eq) {
   const int lane = threadIdx.x & 63;
@@ -641,10 +660,20 @@ __device__ void threshold_radix_lds(const uint32_t* keys, int32_t nsel, uint32_t
     reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
     wave_sync();
     const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
-    for (int32_t j = 0; j < nj; ++j) {
-      const int32_t i = j * 64 + lane;
-      const uint32_t kj = i < nsel ? rank_key(keys[i]) : 0u;
-      if (kj != 0u && (kj & hmask) == prefix) atomicAdd(&hist[(kj >> shift) & 255u], 1u);
+    if constexpr (HK) {
+      for (int32_t j = 0; j < nj; j += 8) {
+        uint32_t kv[8];
+        hbm_keys8(keys, nsel, j, kv);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (kv[q] != 0u && (kv[q] & hmask) == prefix) atomicAdd(&hist[(kv[q] >> shift) & 255u], 1u);
+      }
+    } else {
+      for (int32_t j = 0; j < nj; ++j) {
+        const int32_t i = j * 64 + lane;
+        const uint32_t kj = i < nsel ? rank_key(keys[i]) : 0u;
+        if (kj != 0u && (kj & hmask) == prefix) atomicAdd(&hist[(kj >> shift) & 255u], 1u);
+      }
     }
     wave_sync();
     // lane l holds bins 255-4l (q = 0) down to 252-4l (q = 3); `a0` counts the
@@ -687,45 +716,82 @@ __device__ void threshold_radix_lds(const uint32_t* keys, int32_t nsel, uint32_t
 
 // Exact top-k by one wave over LDS keys[0, nsel) (pin and -inf fill already
 // in place), for rows the candidate bound cannot shrink to kCandCap.
-// `scratch`: 16-byte aligned, max(512, 2*kcap) words.
+// `scratch`: 16-byte aligned, max(512, 2*kcap) words.  HK: keys in HBM.
+template <bool HK = false>
 __device__ void select_wave_exact(const uint32_t* keys, int32_t nsel, int32_t k, int32_t kcap,
                                   int32_t* out_row, uint32_t* scratch) {
   const int lane = threadIdx.x & 63;
   const int32_t nj = (nsel + 63) >> 6;
   uint32_t nvalid = 0;
-  for (int32_t j = 0; j < nj; ++j) {
-    const int32_t i = j * 64 + lane;
-    nvalid += (uint32_t)__popcll(__ballot(i < nsel && rank_key(keys[i]) != 0u));
+  if constexpr (HK) {
+    for (int32_t j = 0; j < nj; j += 8) {
+      uint32_t kv[8];
+      hbm_keys8(keys, nsel, j, kv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) nvalid += (uint32_t)__popcll(__ballot(kv[q] != 0u));
+    }
+  } else {
+    for (int32_t j = 0; j < nj; ++j) {
+      const int32_t i = j * 64 + lane;
+      nvalid += (uint32_t)__popcll(__ballot(i < nsel && rank_key(keys[i]) != 0u));
+    }
   }
   const int32_t keff = (uint32_t)k < nvalid ? k : (int32_t)nvalid;
   if (keff > 0) {
     uint32_t tg = 1u, T = 0u;
     int32_t need_eq = 0;
-    if ((uint32_t)keff < nvalid) threshold_radix_lds(keys, nsel, (uint32_t)keff, scratch, tg, T, need_eq);
+    if ((uint32_t)keff < nvalid)
+      threshold_radix_lds<HK>(keys, nsel, (uint32_t)keff, scratch, tg, T, need_eq);
     // keys >= tg go to sel_* in id order; the first need_eq keys equal to T
     // fill the last slots directly
     uint32_t* sel_key = scratch;
     uint32_t* sel_id = scratch + kcap;
     const int32_t c_gt = keff - need_eq;
     uint32_t pos_gt = 0, pos_eq = 0;
-    for (int32_t j = 0; j < nj; ++j) {
-      const int32_t i = j * 64 + lane;
-      const uint32_t kj = i < nsel ? rank_key(keys[i]) : 0u;
-      const bool is_gt = kj >= tg && kj != 0u;
-      const bool is_eq = need_eq > 0 && kj == T && kj != 0u;
-      const uint64_t m_gt = __ballot(is_gt);
-      const uint64_t m_eq = __ballot(is_eq);
-      if (is_gt) {
-        const uint32_t r = pos_gt + lanes_below(m_gt);
-        sel_key[r] = kj;
-        sel_id[r] = (uint32_t)i;
+    if constexpr (HK) {
+      auto place = [&](int32_t i, uint32_t kj) {  // every lane, in slot order
+        const bool is_gt = kj >= tg && kj != 0u;
+        const bool is_eq = need_eq > 0 && kj == T && kj != 0u;
+        const uint64_t m_gt = __ballot(is_gt);
+        const uint64_t m_eq = __ballot(is_eq);
+        if (is_gt) {
+          const uint32_t r = pos_gt + lanes_below(m_gt);
+          sel_key[r] = kj;
+          sel_id[r] = (uint32_t)i;
+        }
+        if (is_eq) {
+          const uint32_t r = pos_eq + lanes_below(m_eq);
+          if (r < (uint32_t)need_eq) out_row[c_gt + (int32_t)r] = i;
+        }
+        pos_gt += (uint32_t)__popcll(m_gt);
+        pos_eq += (uint32_t)__popcll(m_eq);
+      };
+      for (int32_t j = 0; j < nj; j += 8) {
+        uint32_t kv[8];
+        hbm_keys8(keys, nsel, j, kv);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) place((j + q) * 64 + lane, kv[q]);  // kv = 0 past nsel
       }
-      if (is_eq) {
-        const uint32_t r = pos_eq + lanes_below(m_eq);
-        if (r < (uint32_t)need_eq) out_row[c_gt + (int32_t)r] = i;
+    } else {
+      for (int32_t j = 0; j < nj; ++j) {
+        const int32_t i = j * 64 + lane;
+        const uint32_t kj = i < nsel ? rank_key(keys[i]) : 0u;
+        const bool is_gt = kj >= tg && kj != 0u;
+        const bool is_eq = need_eq > 0 && kj == T && kj != 0u;
+        const uint64_t m_gt = __ballot(is_gt);
+        const uint64_t m_eq = __ballot(is_eq);
+        if (is_gt) {
+          const uint32_t r = pos_gt + lanes_below(m_gt);
+          sel_key[r] = kj;
+          sel_id[r] = (uint32_t)i;
+        }
+        if (is_eq) {
+          const uint32_t r = pos_eq + lanes_below(m_eq);
+          if (r < (uint32_t)need_eq) out_row[c_gt + (int32_t)r] = i;
+        }
+        pos_gt += (uint32_t)__popcll(m_gt);
+        pos_eq += (uint32_t)__popcll(m_eq);
       }
-      pos_gt += (uint32_t)__popcll(m_gt);
-      pos_eq += (uint32_t)__popcll(m_eq);
     }
     wave_sync();
     // order the outright selection: rank = #larger + #equal earlier in id order
@@ -793,7 +859,8 @@ __device__ __forceinline__ LaneKeys lane_keys(const uint32_t* keys, const RowGeo
 
 // Calls f(i, rank key of i) for this lane's keys, in iteration order (the
 // same order for every lane, so f may hold ballots).
-template <class F>
+// HK (keys in HBM): eight keys loaded per step before f sees them.
+template <bool HK = false, class F>
 __device__ __forceinline__ void for_lane_keys(const LaneKeys& lk, const uint32_t* keys,
                                               const RowGeom& g, int wave, int nt, F&& f) {
   const int lane = threadIdx.x & 63;
@@ -801,6 +868,15 @@ __device__ __forceinline__ void for_lane_keys(const LaneKeys& lk, const uint32_t
 #pragma unroll
     for (int j = 0; j < kKeyRegs; ++j)
       if (j < lk.nj) f(wave * 64 + j * nt + lane, lk.v[j]);  // wave-uniform
+  } else if constexpr (HK) {
+    for (int32_t base = wave * 64; base < g.nsel; base += 8 * nt) {  // wave-uniform
+      uint32_t kv[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) kv[q] = select_rank_key(keys, g, base + q * nt + lane);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (base + q * nt < g.nsel) f(base + q * nt + lane, kv[q]);  // wave-uniform
+    }
   } else {
     for (int32_t base = wave * 64; base < g.nsel; base += nt)  // wave-uniform
       f(base + lane, select_rank_key(keys, g, base + lane));
@@ -819,7 +895,7 @@ constexpr int kCtlRemain = 4;   // radix: keys still needed below the prefix's h
 constexpr int kCtlAbove = 5;    // radix: keys above the current bucket
 constexpr int kCtlDone = 6;     // radix: bound final
 
-template <bool WG>
+template <bool WG, bool HK = false>
 __device__ __forceinline__ void bound_radix(const RowGeom& g, int32_t k, const uint32_t* keys,
                                             const LaneKeys& lk, uint32_t* ctl, uint32_t* hist,
                                             int wave, int nw) {
@@ -828,7 +904,7 @@ __device__ __forceinline__ void bound_radix(const RowGeom& g, int32_t k, const u
   uint32_t prefix = 0u, hmask = 0u;
   for (int shift = 24; shift >= 0; shift -= 8) {
     uint32_t nv = 0u;
-    for_lane_keys(lk, keys, g, wave, nt, [&](int32_t, uint32_t rk) {
+    for_lane_keys<HK>(lk, keys, g, wave, nt, [&](int32_t, uint32_t rk) {
       if (rk != 0u && (rk & hmask) == prefix) atomicAdd(&hist[(rk >> shift) & 255u], 1u);
       if (shift == 24) nv += (uint32_t)__popcll(__ballot(rk != 0u));
     });
@@ -975,7 +1051,7 @@ __device__ __forceinline__ uint32_t maxima_bound(uint32_t g0, uint32_t g1, uint3
 // from bound_radix for larger k.  Same-address LDS max serialises per lane
 // on this chip, so the maxima and the bound go through per-wave LDS rows
 // and slots, not atomics.
-template <bool WG, int BOUND, bool KC, bool PRE = false>
+template <bool WG, int BOUND, bool KC, bool PRE = false, bool HK = false>
 __device__ __forceinline__ void select_row_general(const Params& p, const RowGeom& g,
                                                    uint32_t* keys, uint32_t* ctl, uint32_t* area,
                                                    int32_t* out_row, int wave, int nw,
@@ -993,7 +1069,7 @@ __device__ __forceinline__ void select_row_general(const Params& p, const RowGeo
   const LaneKeys lk = PRE ? pre : lane_keys<KC>(keys, g, wave, nt);
 
   if constexpr (BOUND == kBoundRadix) {
-    bound_radix<WG>(g, k, keys, lk, ctl, area, wave, nw);
+    bound_radix<WG, HK>(g, k, keys, lk, ctl, area, wave, nw);
     t0 = ctl[kCtlT0];
     nvalid = ctl[kCtlValid];
   } else if constexpr (BOUND == kBoundGroups128) {
@@ -1003,7 +1079,7 @@ __device__ __forceinline__ void select_row_general(const Params& p, const RowGeo
     // with an odd one (nw <= 8) alternately (two rows per wave).
     uint32_t m0 = 0u, m1 = 0u, nv = 0u;
     const bool two_rows = (nw & 1) != 0;
-    for_lane_keys(lk, keys, g, wave, nt, [&](int32_t i, uint32_t rk) {
+    for_lane_keys<HK>(lk, keys, g, wave, nt, [&](int32_t i, uint32_t rk) {
       if (two_rows && ((i >> 6) & 1)) m1 = umax(m1, rk);
       else m0 = umax(m0, rk);  // one half per wave for an even wave count
       nv += (uint32_t)__popcll(__ballot(rk != 0u));
@@ -1045,7 +1121,7 @@ __device__ __forceinline__ void select_row_general(const Params& p, const RowGeo
     // (A) per lane: maximum of its keys (all in group `lane`), into this
     // wave's row of `area`; per wave: its count of nonzero keys.
     uint32_t tmax = 0u, nv = 0u;
-    for_lane_keys(lk, keys, g, wave, nt, [&](int32_t, uint32_t rk) {
+    for_lane_keys<HK>(lk, keys, g, wave, nt, [&](int32_t, uint32_t rk) {
       tmax = umax(tmax, rk);
       nv += (uint32_t)__popcll(__ballot(rk != 0u));
     });
@@ -1123,6 +1199,18 @@ __device__ __forceinline__ void select_row_general(const Params& p, const RowGeo
           pos += (uint32_t)__popcll(m);
         }
       }
+    } else if constexpr (HK) {
+      for_lane_keys<true>(lk, keys, g, wave, nt, [&](int32_t i, uint32_t rk) {
+        const bool c = rk >= tt;
+        const uint64_t m = __ballot(c);
+        if (m != 0ull) {
+          uint32_t b0 = 0u;
+          if (lane == 0) b0 = atomicAdd(&ctl[kCtlCand], (uint32_t)__popcll(m));
+          b0 = (uint32_t)__builtin_amdgcn_readlane((int)b0, 0);
+          const uint32_t pos = b0 + lanes_below(m);
+          if (c && pos < (uint32_t)kCandCap) cand[pos] = cand_word(rk, (uint32_t)i);
+        }
+      });
     } else {
       for (int32_t base = wave * 64; base < nsel; base += nt) {  // wave-uniform
         const int32_t i = base + lane;
@@ -1164,7 +1252,7 @@ __device__ __forceinline__ void select_row_general(const Params& p, const RowGeo
     wave_sync();
     if (g.pin >= 0 && lane == 0) keys[g.pin] = kKeyPosInf;
     wave_sync();
-    select_wave_exact(keys, nsel, k, p.kcap, out_row, area);
+    select_wave_exact<HK>(keys, nsel, k, p.kcap, out_row, area);
   }
 }
 
@@ -1174,7 +1262,7 @@ __device__ __forceinline__ void select_row_general(const Params& p, const RowGeo
 // (16-byte aligned, max(kAreaMinWords, 2*kcap) words) are this row's LDS
 // scratch, cleared by select_row_prepare before the caller's last barrier.
 // Also writes the optional fp32 score row.
-template <bool WG, bool KC = false, int FB = -1, bool PRE = false>
+template <bool WG, bool KC = false, int FB = -1, bool PRE = false, bool HK = false>
 __device__ __forceinline__ void select_row(const Params& p, int64_t r, const RowGeom& g,
                                            uint32_t* keys, uint32_t* ctl, uint32_t* area,
                                            int wave, int nw, const LaneKeys& pre = LaneKeys{}) {
@@ -1205,15 +1293,18 @@ __device__ __forceinline__ void select_row(const Params& p, int64_t r, const Row
     return;
   }
   if constexpr (FB >= 0) {
-    select_row_general<WG, FB, KC, PRE>(p, g, keys, ctl, area, out_row, wave, nw, pre);
+    select_row_general<WG, FB, KC, PRE, HK>(p, g, keys, ctl, area, out_row, wave, nw, pre);
   } else {
     const int bound = select_bound(k, nw);
     if (bound == kBoundGroups64)
-      select_row_general<WG, kBoundGroups64, KC, PRE>(p, g, keys, ctl, area, out_row, wave, nw, pre);
+      select_row_general<WG, kBoundGroups64, KC, PRE, HK>(p, g, keys, ctl, area, out_row, wave, nw,
+                                                          pre);
     else if (bound == kBoundGroups128)
-      select_row_general<WG, kBoundGroups128, KC, PRE>(p, g, keys, ctl, area, out_row, wave, nw, pre);
+      select_row_general<WG, kBoundGroups128, KC, PRE, HK>(p, g, keys, ctl, area, out_row, wave,
+                                                           nw, pre);
     else
-      select_row_general<WG, kBoundRadix, KC, PRE>(p, g, keys, ctl, area, out_row, wave, nw, pre);
+      select_row_general<WG, kBoundRadix, KC, PRE, HK>(p, g, keys, ctl, area, out_row, wave, nw,
+                                                       pre);
   }
 }
 
@@ -1321,7 +1412,7 @@ __global__ void __launch_bounds__(1024) select_keys_kernel(Params p) {
 // LDS.  The keys past the window ([nvb, nsel)) and the pin are first written
 // into that row, as the exact fallback expects them in place; nothing else
 // reads or writes the row during the call.  Every pass over the keys reads
-// HBM or L2 instead of LDS: correct for any width, not tuned.
+// HBM or L2 instead of LDS, eight loads in flight per lane.
 __global__ void __launch_bounds__(1024) select_keys_hbm_kernel(Params p) {
   extern __shared__ uint32_t smem[];
   const int wave = wave_index();
@@ -1336,7 +1427,7 @@ __global__ void __launch_bounds__(1024) select_keys_hbm_kernel(Params p) {
       keys[b] = b == g.pin ? kKeyPosInf : kKeyNegInf;
     if (threadIdx.x == 0 && g.pin >= 0 && g.pin < g.nvb) keys[g.pin] = kKeyPosInf;
     __syncthreads();  // the workgroup's stores are visible to its loads after it
-    select_row<true>(p, r, g, keys, ctl, area, wave, nw);
+    select_row<true, false, -1, false, true>(p, r, g, keys, ctl, area, wave, nw);
     if (r + gridDim.x < p.items) __syncthreads();
   }
 }
@@ -2008,6 +2099,10 @@ int64_t select_wave_words(int64_t nblocks, int32_t k) {
   return select_keys_words(nblocks) + select_state_words(nblocks, k);
 }
 
+// Largest block count of a selection: the select's slot indices (up to
+// 8 x 1024 past a row's nsel) stay within int32.
+constexpr int64_t kMaxSelectBlocks = (int64_t)INT32_MAX - 8192;
+
 // Rows whose keys and select state exceed one workgroup's LDS: only the
 // split plan holds them, its select reading the keys from the workspace.
 bool keys_past_lds(int64_t nblocks, int32_t k) {
@@ -2117,7 +2212,7 @@ size_t dsa_select_workspace_bytes(int64_t rows, int64_t width, int32_t block_siz
   const int64_t nblocks = cdiv(width, block_size);
   // shapes no plan holds (a row's select state past LDS even with its keys in
   // the workspace): nothing to size
-  if (rows > INT32_MAX || nblocks > INT32_MAX) return 0;
+  if (rows > INT32_MAX || nblocks > kMaxSelectBlocks) return 0;
   if (select_state_words(nblocks, topk_blocks) * 4 > (int64_t)kLdsLimit) return 0;
   if ((uint64_t)ws_row_words(nblocks) > (UINT64_MAX / 8u) / (uint64_t)rows) return 0;  // no size_t
   return kCountBytes + (size_t)rows * (size_t)ws_row_words(nblocks) * 4u;
@@ -2302,7 +2397,7 @@ dsa_status_t dsa_select_candidate_blocks_plan(
   if (!logits || !row_ke) return DSA_ERR_INVALID_ARG;
   if (misaligned(logits, 4) || (scores_out && misaligned(scores_out, 4)))
     return DSA_ERR_INVALID_ARG;
-  if (nblocks > INT32_MAX) return DSA_ERR_UNSUPPORTED;
+  if (nblocks > kMaxSelectBlocks) return DSA_ERR_UNSUPPORTED;
   const int64_t ww = select_wave_words(nblocks, topk_blocks);
   // keys past LDS: the split plan with its keys left in the workspace
   const bool hbm_keys = keys_past_lds(nblocks, topk_blocks);
