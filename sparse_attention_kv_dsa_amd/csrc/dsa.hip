@@ -632,25 +632,6 @@ __device__ __forceinline__ void rank_candidates_split(const uint64_t* cand, int3
 // Radix select (8-bit digits from the top) over the LDS rank keys of one
 // wave's slot array (slot j of lane l is key j*64 + l): the selection is every
 // key >= tg, then the first need_eq keys equal to T in id order.
-// Rank keys of slots [j, j + 8) of one wave's key array (slot j of lane l is
-// key j*64 + l), 0 past nsel, all eight loads issued before any is used: for
-// keys in HBM, where one load per step would wait out its whole latency.
-// nsel >= 1 (keys[0] is read in place of the slots past it).
-__device__ __forceinline__ void hbm_keys8(const uint32_t* keys, int32_t nsel, int32_t j,
-                                          uint32_t (&kv)[8]) {
-  const int lane = threadIdx.x & 63;
-  uint32_t raw[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int32_t i = (j + q) * 64 + lane;
-    raw[q] = keys[i < nsel ? i : 0];
-  }
-#pragma unroll
-  for (int q = 0; q < 8; ++q) kv[q] = (j + q) * 64 + lane < nsel ? rank_key(raw[q]) : 0u;
-}
-
-// HK: the keys sit in HBM (eight loads in flight per step), else in LDS.
-template <bool HK = false>
 __device__ void threshold_radix_lds(const uint32_t* keys, int32_t nsel, uint32_t keff,
                                     uint32_t* hist, uint32_t& tg, uint32_t& T, int32_t& need_eq) {
   const int lane = threadIdx.x & 63;
@@ -660,20 +641,10 @@ __device__ void threshold_radix_lds(const uint32_t* keys, int32_t nsel, uint32_t
     reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
     wave_sync();
     const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
-    if constexpr (HK) {
-      for (int32_t j = 0; j < nj; j += 8) {
-        uint32_t kv[8];
-        hbm_keys8(keys, nsel, j, kv);
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (kv[q] != 0u && (kv[q] & hmask) == prefix) atomicAdd(&hist[(kv[q] >> shift) & 255u], 1u);
-      }
-    } else {
-      for (int32_t j = 0; j < nj; ++j) {
-        const int32_t i = j * 64 + lane;
-        const uint32_t kj = i < nsel ? rank_key(keys[i]) : 0u;
-        if (kj != 0u && (kj & hmask) == prefix) atomicAdd(&hist[(kj >> shift) & 255u], 1u);
-      }
+    for (int32_t j = 0; j < nj; ++j) {
+      const int32_t i = j * 64 + lane;
+      const uint32_t kj = i < nsel ? rank_key(keys[i]) : 0u;
+      if (kj != 0u && (kj & hmask) == prefix) atomicAdd(&hist[(kj >> shift) & 255u], 1u);
     }
     wave_sync();
     // lane l holds bins 255-4l (q = 0) down to 252-4l (q = 3); `a0` counts the
@@ -716,82 +687,45 @@ __device__ void threshold_radix_lds(const uint32_t* keys, int32_t nsel, uint32_t
 
 // Exact top-k by one wave over LDS keys[0, nsel) (pin and -inf fill already
 // in place), for rows the candidate bound cannot shrink to kCandCap.
-// `scratch`: 16-byte aligned, max(512, 2*kcap) words.  HK: keys in HBM.
-template <bool HK = false>
+// `scratch`: 16-byte aligned, max(512, 2*kcap) words.
 __device__ void select_wave_exact(const uint32_t* keys, int32_t nsel, int32_t k, int32_t kcap,
                                   int32_t* out_row, uint32_t* scratch) {
   const int lane = threadIdx.x & 63;
   const int32_t nj = (nsel + 63) >> 6;
   uint32_t nvalid = 0;
-  if constexpr (HK) {
-    for (int32_t j = 0; j < nj; j += 8) {
-      uint32_t kv[8];
-      hbm_keys8(keys, nsel, j, kv);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) nvalid += (uint32_t)__popcll(__ballot(kv[q] != 0u));
-    }
-  } else {
-    for (int32_t j = 0; j < nj; ++j) {
-      const int32_t i = j * 64 + lane;
-      nvalid += (uint32_t)__popcll(__ballot(i < nsel && rank_key(keys[i]) != 0u));
-    }
+  for (int32_t j = 0; j < nj; ++j) {
+    const int32_t i = j * 64 + lane;
+    nvalid += (uint32_t)__popcll(__ballot(i < nsel && rank_key(keys[i]) != 0u));
   }
   const int32_t keff = (uint32_t)k < nvalid ? k : (int32_t)nvalid;
   if (keff > 0) {
     uint32_t tg = 1u, T = 0u;
     int32_t need_eq = 0;
-    if ((uint32_t)keff < nvalid)
-      threshold_radix_lds<HK>(keys, nsel, (uint32_t)keff, scratch, tg, T, need_eq);
+    if ((uint32_t)keff < nvalid) threshold_radix_lds(keys, nsel, (uint32_t)keff, scratch, tg, T, need_eq);
     // keys >= tg go to sel_* in id order; the first need_eq keys equal to T
     // fill the last slots directly
     uint32_t* sel_key = scratch;
     uint32_t* sel_id = scratch + kcap;
     const int32_t c_gt = keff - need_eq;
     uint32_t pos_gt = 0, pos_eq = 0;
-    if constexpr (HK) {
-      auto place = [&](int32_t i, uint32_t kj) {  // every lane, in slot order
-        const bool is_gt = kj >= tg && kj != 0u;
-        const bool is_eq = need_eq > 0 && kj == T && kj != 0u;
-        const uint64_t m_gt = __ballot(is_gt);
-        const uint64_t m_eq = __ballot(is_eq);
-        if (is_gt) {
-          const uint32_t r = pos_gt + lanes_below(m_gt);
-          sel_key[r] = kj;
-          sel_id[r] = (uint32_t)i;
-        }
-        if (is_eq) {
-          const uint32_t r = pos_eq + lanes_below(m_eq);
-          if (r < (uint32_t)need_eq) out_row[c_gt + (int32_t)r] = i;
-        }
-        pos_gt += (uint32_t)__popcll(m_gt);
-        pos_eq += (uint32_t)__popcll(m_eq);
-      };
-      for (int32_t j = 0; j < nj; j += 8) {
-        uint32_t kv[8];
-        hbm_keys8(keys, nsel, j, kv);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) place((j + q) * 64 + lane, kv[q]);  // kv = 0 past nsel
+    for (int32_t j = 0; j < nj; ++j) {
+      const int32_t i = j * 64 + lane;
+      const uint32_t kj = i < nsel ? rank_key(keys[i]) : 0u;
+      const bool is_gt = kj >= tg && kj != 0u;
+      const bool is_eq = need_eq > 0 && kj == T && kj != 0u;
+      const uint64_t m_gt = __ballot(is_gt);
+      const uint64_t m_eq = __ballot(is_eq);
+      if (is_gt) {
+        const uint32_t r = pos_gt + lanes_below(m_gt);
+        sel_key[r] = kj;
+        sel_id[r] = (uint32_t)i;
       }
-    } else {
-      for (int32_t j = 0; j < nj; ++j) {
-        const int32_t i = j * 64 + lane;
-        const uint32_t kj = i < nsel ? rank_key(keys[i]) : 0u;
-        const bool is_gt = kj >= tg && kj != 0u;
-        const bool is_eq = need_eq > 0 && kj == T && kj != 0u;
-        const uint64_t m_gt = __ballot(is_gt);
-        const uint64_t m_eq = __ballot(is_eq);
-        if (is_gt) {
-          const uint32_t r = pos_gt + lanes_below(m_gt);
-          sel_key[r] = kj;
-          sel_id[r] = (uint32_t)i;
-        }
-        if (is_eq) {
-          const uint32_t r = pos_eq + lanes_below(m_eq);
-          if (r < (uint32_t)need_eq) out_row[c_gt + (int32_t)r] = i;
-        }
-        pos_gt += (uint32_t)__popcll(m_gt);
-        pos_eq += (uint32_t)__popcll(m_eq);
+      if (is_eq) {
+        const uint32_t r = pos_eq + lanes_below(m_eq);
+        if (r < (uint32_t)need_eq) out_row[c_gt + (int32_t)r] = i;
       }
+      pos_gt += (uint32_t)__popcll(m_gt);
+      pos_eq += (uint32_t)__popcll(m_eq);
     }
     wave_sync();
     // order the outright selection: rank = #larger + #equal earlier in id order
@@ -895,7 +829,10 @@ constexpr int kCtlRemain = 4;   // radix: keys still needed below the prefix's h
 constexpr int kCtlAbove = 5;    // radix: keys above the current bucket
 constexpr int kCtlDone = 6;     // radix: bound final
 
-template <bool WG, bool HK = false>
+// EXACT: no early stop, every digit fixed: T0 is then the keff-th largest
+// key, kCtlAbove the count of keys above it and kCtlRemain the keys equal to
+// it that complete the keff.
+template <bool WG, bool HK = false, bool EXACT = false>
 __device__ __forceinline__ void bound_radix(const RowGeom& g, int32_t k, const uint32_t* keys,
                                             const LaneKeys& lk, uint32_t* ctl, uint32_t* hist,
                                             int wave, int nw) {
@@ -958,7 +895,7 @@ __device__ __forceinline__ void bound_radix(const RowGeom& g, int32_t k, const u
           ctl[kCtlPrefix] = np;
           ctl[kCtlRemain] = remaining - above_d;
           ctl[kCtlAbove] = na;
-          if (na + cnt_d <= (uint32_t)kCandCap || shift == 0) {
+          if ((!EXACT && na + cnt_d <= (uint32_t)kCandCap) || shift == 0) {
             ctl[kCtlT0] = np;  // keys >= np: the na above plus the bucket's cnt_d
             ctl[kCtlDone] = 1u;
           }
@@ -1045,6 +982,81 @@ __device__ __forceinline__ uint32_t maxima_bound(uint32_t g0, uint32_t g1, uint3
   return t;
 }
 
+// The exact select of a row whose keys sit in HBM (select_keys_hbm_kernel),
+// for rows the candidate bound cannot shrink to kCandCap (k above it, or
+// ties at the bound), by the whole workgroup: radix passes fix the keff-th
+// largest key T, the keys above T (fewer than keff, so they fit the area)
+// are ranked by count, and the keys equal to T fill the remaining slots in
+// id order, 8 x nt ids per step until enough are placed.  Called by every
+// wave after the compaction's barrier.
+template <bool WG>
+__device__ void exact_select_hbm(const RowGeom& g, int32_t k, const uint32_t* keys,
+                                 const LaneKeys& lk, uint32_t* ctl, uint32_t* area,
+                                 int32_t* out_row, int wave, int nw) {
+  const int lane = threadIdx.x & 63;
+  const int tid = wave * 64 + lane;
+  const int nt = nw * 64;
+  row_barrier<WG>();  // every wave has read the candidate count
+  for (int t = tid; t < 256; t += nt) area[t] = 0u;  // the radix histogram
+  if (tid == 0) {
+    ctl[kCtlValid] = 0u;
+    ctl[kCtlCand] = 0u;
+    ctl[kCtlDone] = 0u;
+  }
+  row_barrier<WG>();
+  bound_radix<WG, true, true>(g, k, keys, lk, ctl, area, wave, nw);
+  const uint32_t nvalid = ctl[kCtlValid];
+  const int32_t keff = (uint32_t)k < nvalid ? k : (int32_t)nvalid;
+  if (keff > 0) {  // workgroup-uniform
+    const uint32_t T = ctl[kCtlT0];
+    const uint32_t above = ctl[kCtlAbove];  // keys > T: fewer than keff
+    const uint32_t need_eq = (uint32_t)keff - above;
+    uint64_t* cand = reinterpret_cast<uint64_t*>(area);
+    for_lane_keys<true>(lk, keys, g, wave, nt, [&](int32_t i, uint32_t rk) {
+      const bool c = rk > T;
+      const uint64_t m = __ballot(c);
+      if (m != 0ull) {
+        uint32_t b0 = 0u;
+        if (lane == 0) b0 = atomicAdd(&ctl[kCtlCand], (uint32_t)__popcll(m));
+        b0 = (uint32_t)__builtin_amdgcn_readlane((int)b0, 0);
+        if (c) cand[b0 + lanes_below(m)] = cand_word(rk, (uint32_t)i);
+      }
+    });
+    row_barrier<WG>();
+    rank_candidates(cand, (int32_t)above, (int32_t)above, out_row, wave, nw);
+    row_barrier<WG>();  // the rank has read the candidates: the area takes the tie counts
+    uint32_t* wcnt = area;  // [8][16]: the ties of each slice and wave of a step
+    uint32_t run = 0u;      // ties placed by the earlier steps
+    for (int32_t base = 0; base < g.nsel && run < need_eq; base += 8 * nt) {  // workgroup-uniform
+      // slice q of the step holds ids base + q*nt + [0, nt), wave w its w-th 64
+      uint32_t kv[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) kv[q] = select_rank_key(keys, g, base + q * nt + wave * 64 + lane);
+      uint64_t m[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        m[q] = __ballot(kv[q] == T);  // 0 past nsel, and T > 0
+        if (lane == 0) wcnt[q * 16 + wave] = (uint32_t)__popcll(m[q]);
+      }
+      row_barrier<WG>();
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        uint32_t before = 0u, total = 0u;
+        for (int w = 0; w < nw; ++w) {
+          const uint32_t c = wcnt[q * 16 + w];
+          before += w < wave ? c : 0u;
+          total += c;
+        }
+        const uint32_t pos = run + before + lanes_below(m[q]);
+        if (kv[q] == T && pos < need_eq) out_row[above + pos] = base + q * nt + wave * 64 + lane;
+        run += total;
+      }
+      row_barrier<WG>();  // the counts are rewritten by the next step
+    }
+  }
+  for (int32_t j = keff + tid; j < k; j += nt) out_row[j] = -1;
+}
+
 // The general path of select_row (nsel > 64).  The candidate bound T0 comes
 // from NG group maxima (NG = 64 or 128), group l holding the keys i with
 // i mod NG == l: T0 = the keff-th largest group maximum (keff <= NG), or
@@ -1067,6 +1079,12 @@ __device__ __forceinline__ void select_row_general(const Params& p, const RowGeo
   uint64_t* cand = reinterpret_cast<uint64_t*>(area + (past ? nw * 64 : 0));
   uint32_t t0, nvalid;
   const LaneKeys lk = PRE ? pre : lane_keys<KC>(keys, g, wave, nt);
+  if constexpr (HK) {
+    if (k > kCandCap) {  // no bound leaves k or more keys within the store: exact at once
+      exact_select_hbm<WG>(g, k, keys, lk, ctl, area, out_row, wave, nw);
+      return;
+    }
+  }
 
   if constexpr (BOUND == kBoundRadix) {
     bound_radix<WG, HK>(g, k, keys, lk, ctl, area, wave, nw);
@@ -1238,6 +1256,8 @@ __device__ __forceinline__ void select_row_general(const Params& p, const RowGeo
   } else if (ncand <= kCandCap) {
     rank_candidates<!PRE>(cand, ncand, keff, out_row, wave, nw);
     for (int32_t j = keff + tid; j < k; j += nt) out_row[j] = -1;
+  } else if constexpr (HK) {
+    exact_select_hbm<WG>(g, k, keys, lk, ctl, area, out_row, wave, nw);
   } else {
     if constexpr (PRE) {  // the exact select reads the keys from LDS
 #pragma unroll
@@ -1252,7 +1272,7 @@ __device__ __forceinline__ void select_row_general(const Params& p, const RowGeo
     wave_sync();
     if (g.pin >= 0 && lane == 0) keys[g.pin] = kKeyPosInf;
     wave_sync();
-    select_wave_exact<HK>(keys, nsel, k, p.kcap, out_row, area);
+    select_wave_exact(keys, nsel, k, p.kcap, out_row, area);
   }
 }
 
@@ -1408,11 +1428,11 @@ __global__ void __launch_bounds__(1024) select_keys_kernel(Params p) {
 
 // Plan "split", second kernel for rows whose keys exceed one workgroup's
 // LDS: the select reads the keys where the first kernel left them (the row
-// of the workspace) and keeps only its control words and candidate area in
-// LDS.  The keys past the window ([nvb, nsel)) and the pin are first written
-// into that row, as the exact fallback expects them in place; nothing else
-// reads or writes the row during the call.  Every pass over the keys reads
-// HBM or L2 instead of LDS, eight loads in flight per lane.
+// of the workspace, [0, nvb); the pin and the blocks past the window are
+// applied as the keys are read) and keeps only its control words and
+// candidate area in LDS.  Every pass over the keys reads HBM or L2 instead
+// of LDS, eight loads in flight per lane, and the exact select runs on the
+// whole workgroup (exact_select_hbm).
 __global__ void __launch_bounds__(1024) select_keys_hbm_kernel(Params p) {
   extern __shared__ uint32_t smem[];
   const int wave = wave_index();
@@ -1421,12 +1441,9 @@ __global__ void __launch_bounds__(1024) select_keys_hbm_kernel(Params p) {
   uint32_t* area = ctl + kCtlWords;
   for (int64_t r = blockIdx.x; r < p.items; r += gridDim.x) {
     const RowGeom g = row_geom(p, r, true);
-    uint32_t* keys = p.ws_keys + r * p.ws_ld;  // nsel <= nblocks <= ws_ld words
+    uint32_t* keys = p.ws_keys + r * p.ws_ld;  // only read
     select_row_prepare(ctl, area, threadIdx.x, blockDim.x);
-    for (int32_t b = g.nvb + (int32_t)threadIdx.x; b < g.nsel; b += (int32_t)blockDim.x)
-      keys[b] = b == g.pin ? kKeyPosInf : kKeyNegInf;
-    if (threadIdx.x == 0 && g.pin >= 0 && g.pin < g.nvb) keys[g.pin] = kKeyPosInf;
-    __syncthreads();  // the workgroup's stores are visible to its loads after it
+    __syncthreads();
     select_row<true, false, -1, false, true>(p, r, g, keys, ctl, area, wave, nw);
     if (r + gridDim.x < p.items) __syncthreads();
   }
