@@ -159,9 +159,10 @@ size_t dsa_select_workspace_bytes(int64_t rows, int64_t width, int32_t block_siz
  *   2*kcap))) > 65536, with kcap = max(1, min(topk_blocks, nblocks)) (a
  *   row's keys and select state exceed one workgroup's 64 KiB of LDS), only
  *   the split plan holds the rows: its select reads the keys from the
- *   workspace instead of LDS (correct, not tuned: every pass over the keys
- *   reads HBM or L2).  The automatic plan takes it, and returns
- *   DSA_ERR_WORKSPACE when the workspace is missing or too small.
+ *   workspace instead of LDS (every pass over the keys reads HBM or L2, so
+ *   these rows select slower than rows held in LDS).  The automatic plan
+ *   takes it, and returns DSA_ERR_WORKSPACE when the workspace is missing
+ *   or too small.
  * Unsupported: 4 * (48 + roundup4(max(1024, 2*kcap))) > 65536 (the select
  *   state alone exceeds LDS, topk_blocks above 8168), rows past LDS under a
  *   plan other than the split plan, more than 2^31 - 1 rows or
