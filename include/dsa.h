@@ -282,7 +282,9 @@ const char* dsa_status_string(int status);
  * Invalid: negative sizes, row_repeat < 1, global_block_size < 1,
  *   ld_scores < nscore (nscore > 0), ld_out < topk_blocks, null or
  *   misaligned pointers when there is work.
- * Unsupported: nblocks above the LDS limit of dsa_select_candidate_blocks.
+ * Unsupported: 4 * (roundup4(nblocks) + 48 + roundup4(max(1024, 2*kcap))) > 65536,
+ *   kcap = max(1, min(topk_blocks, nblocks)): a row's scores and select state
+ *   must fit in one workgroup's LDS (there is no workspace to hold them).
  */
 dsa_status_t dsa_select_from_scores(const float* scores, int64_t rows, int64_t nscore,
                                     int64_t ld_scores, int64_t max_global_blocks,
