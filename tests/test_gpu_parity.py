@@ -708,6 +708,43 @@ def test_rows_past_lds(plan):
             assert np.array_equal(o.cpu().numpy(), oracle_select(w)[0])
 
 
+def test_random_shapes_past_lds():
+    """48 random shapes whose rows exceed LDS: B 1-16, up to 200,000 columns,
+    k from 0 to 2048 (both sides of the 256-word candidate store), ties,
+    all-equal rows, NaN, -inf, windows with starts, unaligned rows, the
+    automatic plan and the split plan with assorted chunks."""
+    for seed in range(48):
+        rng = np.random.default_rng(9000 + seed)
+        B = int(rng.choice([1, 2, 3, 4, 8, 16]))
+        width = int(rng.integers(15313 * B, max(15313 * B + 1, 200000)))
+        rows = int(rng.integers(1, 12))
+        k = int(rng.choice([0, 1, 5, 32, 33, 64, 65, 200, 256, 257, 300, 1000, 2048]))
+        R = int(rng.integers(1, 4))
+        g = -(-rows // R)
+        x = rng.standard_normal((rows, width), dtype=np.float32)
+        if seed % 4 == 1:
+            x = np.rint(x * 4) / 4
+        elif seed % 4 == 2:
+            x = np.rint(x * 64) / 64
+        elif seed % 4 == 3:
+            x[:] = np.float32(0.25)
+        if seed % 5 == 0:
+            x[rng.random((rows, width)) < 1e-4] = np.nan
+        if seed % 7 == 0:
+            x[rng.random((rows, width)) < 0.3] = -np.inf
+        x = x.astype(np.float32)
+        ks = None if seed % 2 else rng.integers(-3, width // 8, size=g).astype(np.int32)
+        base = np.zeros(g, np.int64) if ks is None else ks.astype(np.int64)
+        ke = np.clip(base + rng.integers(-5, width + 20, size=g), -3, width + 9).astype(np.int32)
+        plan = (0, 0, 2)[seed % 3]
+        w = workloads.Workload(f"past-lds-random-{seed}", x, ks, ke, B, k, R)
+        got, sc = gpu_select(w, plan, (0, 1, 64, 5000)[seed % 4] if plan == 2 else 0,
+                             ld_pad=(0, 4, 1)[seed % 3], offset=(0, 0, 1, 4)[seed % 4],
+                             ld_out_pad=2)
+        exp_out, exp_sc = oracle_select(w)
+        assert_same(got, sc, exp_out, exp_sc, f"seed {seed} plan {plan} {w.describe()}")
+
+
 def test_rows_past_4_gib():
     """Row offsets past 2^32 bytes: 72 rows 64 MB apart (4.6 GB of logits,
     NaN after each row's first 6000 columns), so the last rows start beyond
